@@ -1,0 +1,173 @@
+/*
+ * int8mm.h -- C ABI of the LLM.int8() mixed-precision decomposed matmul on
+ * AMD Instinct MI355X (gfx950).
+ *
+ *     Y = X_O . W_O  (fp16 operands, fp32 accumulation)
+ *       + dequant( int8(X_R) . int8(W_R) )
+ *
+ * O is the set of input-feature columns of X whose largest |x| over the rows
+ * of this call exceeds the threshold, R the rest ("LLM.int8() notes"
+ * (zwxr.cn), section 2.3, decomposition formula and threshold).  W is
+ * quantized once per output channel with absmax/127 scales ("PyTorch 2.9
+ * supports LLM.int8()" (yongjin360.com), section 1); X is quantized on every
+ * call, one absmax/127 scale per row taken over the R columns (same page,
+ * section 2, dynamic activation quantization).  Codes round half to even and
+ * clamp to [-127, 127].  The int8 product accumulates exactly in int32, is
+ * rescaled by a_x[m] * a_w[n] / 127^2 and the outlier product is added
+ * (same page, section 3: the two parts are merged).  W_O is the dequantized
+ * int8 weight fp16(fp32(Wq * a_w) / 127): the prepared weight holds no fp16
+ * copy of W.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device.
+ *     The caller owns all memory; the library allocates nothing, never
+ *     synchronises the host and enqueues all work on `stream` (0 = the null
+ *     stream).
+ *   - float16 data is passed as IEEE binary16 bit patterns (int8mm_half).
+ *   - All argument checks run on the host before anything is enqueued; a
+ *     failed check returns a negative status and enqueues nothing.
+ *   - HIP launch failures return INT8MM_EHIP; the error text is available
+ *     from int8mm_last_hip_error() on the calling thread.
+ *   - No global mutable state: calls on different streams with different
+ *     workspaces may run concurrently.  Two calls that share a workspace
+ *     must be ordered (e.g. on one stream).
+ *   - Row-major layouts.  `ldk` below is int8_weight_ld(K): K rounded up to a
+ *     multiple of 64; padding columns hold zeros.
+ */
+#ifndef INT8MM_H
+#define INT8MM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* IEEE binary16 bit pattern. */
+typedef uint16_t int8mm_half;
+
+/* Exported entry points (the library is built with hidden visibility). */
+#define INT8MM_API __attribute__((visibility("default")))
+
+/* Status codes (returned; nothing throws across the ABI). */
+#define INT8MM_OK 0
+#define INT8MM_EINVAL (-1)     /* null pointer, NaN or negative threshold   */
+#define INT8MM_ESHAPE (-2)     /* negative dimension or K > INT8MM_MAX_K     */
+#define INT8MM_EWORKSPACE (-3) /* workspace null, too small or misaligned    */
+#define INT8MM_EHIP (-4)       /* a HIP launch failed                        */
+
+/* Largest K for which every int32 accumulator |sum_k q_x q_w| <= 127*127*K
+ * fits in int32 (127*127*133144 = 2147479576 < 2^31). */
+#define INT8MM_MAX_K 133144
+
+/* Rows of X up to which int8_matmul takes the memory-bound decode kernel
+ * (one pass over the int8 weight); larger M takes the MFMA tile GEMM. */
+#define INT8MM_DECODE_MAX_M 16
+
+/* Row stride, in elements, of every [.][ldk] buffer: K rounded up to 64.
+ * Returns -1 for K < 0. */
+INT8MM_API int64_t int8_weight_ld(int64_t K);
+
+/*
+ * int8_prepare_weight -- one-time per-output-channel quantization of W.
+ * ("PyTorch 2.9 supports LLM.int8()", section 1: scale[n] = max|W[n,:]|/127,
+ * int8 weight = round(W / scale); run once, the page's "first inference is
+ * slower" one-time quantization.)
+ *
+ *   W        [N][K]   float16, row-major (nn.Linear [out_features][in_features]).
+ *   Wq       [N][ldk] int8 out: Wq[n][k] = clamp(rne(fp32(127*W[n][k]) / a_w[n]),
+ *                     -127, 127), 0 where a_w[n] == 0; columns K..ldk-1 are 0.
+ *   w_scale  [N]      float out: a_w[n] = max_k |W[n][k]| (the absmax itself,
+ *                     not divided by 127).
+ * N == 0 or K == 0 is a valid no-op (returns INT8MM_OK, nothing enqueued,
+ * except that with K == 0 and N > 0 the scales are set to 0).
+ * Errors: EINVAL (null pointer with N > 0), ESHAPE (N < 0, K < 0, K > MAX_K),
+ * EHIP.
+ */
+INT8MM_API int int8_prepare_weight(const int8mm_half* W, int64_t N, int64_t K,
+                        int8_t* Wq, float* w_scale, hipStream_t stream);
+
+/*
+ * Bytes of device workspace int8_matmul / int8_matmul_stages need for this
+ * shape (sized for the worst case |O| = K).  Returns 0 for an invalid shape.
+ * The workspace must be 256-byte aligned.  Its contents on entry do not
+ * matter; on return they are unspecified.
+ */
+INT8MM_API size_t int8_matmul_workspace_size(int64_t M, int64_t K, int64_t N);
+
+/*
+ * int8_matmul -- Y = decomposed int8 matmul of X with the prepared weight.
+ *
+ *   X         [M][K]   float16 activations (row-major, row stride K).
+ *   Wq        [N][ldk] int8, w_scale [N] float: from int8_prepare_weight.
+ *   threshold          outlier threshold t >= 0 (+inf allowed): column k is an
+ *                      outlier when max_m |X[m][k]| > t (strict).  t = 0 sends
+ *                      every non-zero column to the fp16 path; t = +inf none.
+ *   Y         [M][N]   float16 out.
+ *   workspace          >= int8_matmul_workspace_size(M, K, N) bytes.
+ * M == 0 or N == 0: nothing to do, returns INT8MM_OK.  K == 0: Y is zeroed.
+ * Errors: EINVAL (null pointer, NaN or negative threshold), ESHAPE,
+ * EWORKSPACE, EHIP.
+ */
+INT8MM_API int int8_matmul(const int8mm_half* X, int64_t M, int64_t K,
+                const int8_t* Wq, const float* w_scale, int64_t N,
+                float threshold, int8mm_half* Y,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * int8_matmul_stages -- the same kernels as int8_matmul for this shape, with
+ * every intermediate of the method exposed (for verification).  Every output
+ * pointer is optional (NULL = not wanted).  When C is given the matmul kernel
+ * runs in its int32-output mode and Y is not produced; Y is produced only
+ * when C is NULL and Y is not.
+ *
+ *   mask        [K]      uint8 out: 1 where column k is an outlier.
+ *   n_outliers  [1]      int32 out: |O|.
+ *   outlier_idx [K]      int32 out: O in ascending order (first |O| valid).
+ *   Xq          [M][ldk] int8 out: quantized X, 0 in outlier and pad columns.
+ *   x_scale     [M]      float out: a_x[m] = max over R of |X[m][k]| (0 if none).
+ *   X_O         [M][ldk] float16 out: X_O[m][j] = X[m][O_j] for j < |O|, then
+ *                        zeros up to the next multiple of 64 columns.
+ *   W_O         [N][ldk] float16 out: W_O[n][j] = fp16(fp32(Wq[n][O_j]*a_w[n])/127)
+ *                        for j < |O|, then zeros up to the next multiple of 64.
+ *   C           [M][N]   int32 out: C[m][n] = sum_k Xq[m][k] * Wq[n][k].
+ *   Y           [M][N]   float16 out.
+ * Errors as int8_matmul.
+ */
+INT8MM_API int int8_matmul_stages(const int8mm_half* X, int64_t M, int64_t K,
+                       const int8_t* Wq, const float* w_scale, int64_t N,
+                       float threshold,
+                       uint8_t* mask, int32_t* n_outliers, int32_t* outlier_idx,
+                       int8_t* Xq, float* x_scale, int8mm_half* X_O,
+                       int8mm_half* W_O, int32_t* C, int8mm_half* Y,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * int8_matmul_profiled -- int8_matmul, plus two caller-created HIP events
+ * recorded on `stream` immediately before and after the launch of the
+ * matmul kernel (the tile GEMM, or the decode kernel for M <= 16), so that
+ * its own duration can be read with hipEventElapsedTime.  Either event may
+ * be NULL.  Same computation, arguments and errors as int8_matmul.
+ */
+INT8MM_API int int8_matmul_profiled(const int8mm_half* X, int64_t M, int64_t K,
+                const int8_t* Wq, const float* w_scale, int64_t N,
+                float threshold, int8mm_half* Y,
+                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                hipEvent_t matmul_start, hipEvent_t matmul_stop);
+
+/* Static text for a status code. */
+INT8MM_API const char* int8mm_strerror(int status);
+
+/* Text of the last HIP error seen by this library on the calling thread
+ * ("" if none). */
+INT8MM_API const char* int8mm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT8MM_H */

@@ -1,0 +1,27 @@
+"""LLM.int8() mixed-precision decomposed matmul for AMD Instinct MI355X (gfx950).
+
+    Y = X_O . W_O (fp16) + dequant(int8(X_R) . int8(W_R))
+
+The computation lives in hand-written HIP kernels behind a C ABI
+(``include/int8mm.h``, built into ``libint8mm.so``); this package is the thin
+Python binding over it, with torch used only for device memory and streams.
+
+    import int8_quantized_matmul_col_amd as mm
+    Wq, w_scale = mm.int8_prepare_weight(W)          # once per weight
+    Y = mm.int8_matmul(X, Wq, w_scale, threshold=6.0)
+"""
+
+from .binding import (  # noqa: F401
+    DEFAULT_THRESHOLD,
+    INT8MM_DECODE_MAX_M,
+    INT8MM_MAX_K,
+    Int8mmError,
+    int8_matmul,
+    int8_matmul_profiled,
+    int8_matmul_stages,
+    int8_matmul_workspace_size,
+    int8_prepare_weight,
+    int8_weight_ld,
+    load,
+    workspace_for,
+)

@@ -1,0 +1,214 @@
+// C ABI of the decomposed int8 matmul (include/int8mm.h): argument checks,
+// workspace carving and the launch sequence.  Everything here runs on the
+// host; all device work is enqueued on the caller's stream, nothing is
+// allocated and the host never waits on the device.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "int8mm.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_hip_error[256] = "";
+
+int hip_fail(hipError_t e) {
+  snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return INT8MM_EHIP;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxRows = (int64_t)1 << 30;  // M and N: int32 indexing in the kernels
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+int64_t ld_of(int64_t K) { return (K + 63) / 64 * 64; }
+
+// Byte offsets of the workspace regions for one shape.
+struct Layout {
+  int64_t ldk = 0;
+  bool decode = false;
+  int rc = 0;  // row chunks of the column-absmax pass (prefill path)
+  size_t part = 0, bits = 0, count = 0, xscale = 0, xq = 0, xo = 0, wo = 0, total = 0;
+};
+
+Layout make_layout(int64_t M, int64_t K, int64_t N) {
+  Layout L;
+  L.ldk = ld_of(K);
+  L.decode = M <= INT8MM_DECODE_MAX_M;
+  L.rc = L.decode ? 0 : (int)((M + i8mm::kColmaxRowsPerChunk - 1) / i8mm::kColmaxRowsPerChunk);
+  size_t off = 0;
+  L.part = off;   off += align_up((size_t)L.rc * L.ldk * 2);
+  L.bits = off;   off += align_up((size_t)(L.ldk / 32) * 4);
+  L.count = off;  off += kAlign;
+  L.xscale = off; off += align_up((size_t)M * 4);
+  L.xq = off;     off += align_up((size_t)M * L.ldk);
+  L.xo = off;     off += L.decode ? 0 : align_up((size_t)M * L.ldk * 2);
+  L.wo = off;     off += L.decode ? 0 : align_up((size_t)N * L.ldk * 2);
+  L.total = off < kAlign ? kAlign : off;
+  return L;
+}
+
+int check_shape(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 0 || N < 0) return INT8MM_ESHAPE;
+  if (K > INT8MM_MAX_K || M > kMaxRows || N > kMaxRows) return INT8MM_ESHAPE;
+  return INT8MM_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+struct Outputs {
+  uint8_t* mask = nullptr;
+  int32_t* n_outliers = nullptr;
+  int32_t* outlier_idx = nullptr;
+  int8_t* Xq = nullptr;
+  float* x_scale = nullptr;
+  uint16_t* X_O = nullptr;
+  uint16_t* W_O = nullptr;
+  int32_t* C = nullptr;
+  uint16_t* Y = nullptr;
+};
+
+int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* w_scale, int64_t N,
+        float threshold, const Outputs& out, bool stages, void* ws, size_t ws_bytes,
+        hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
+  int st = check_shape(M, K, N);
+  if (st != INT8MM_OK) return st;
+  if (isnan(threshold) || threshold < 0.0f) return INT8MM_EINVAL;
+  if (M == 0 || N == 0) return INT8MM_OK;
+  if (!stages && out.Y == nullptr) return INT8MM_EINVAL;
+  if (K > 0 && (X == nullptr || Wq == nullptr)) return INT8MM_EINVAL;
+  if (w_scale == nullptr) return INT8MM_EINVAL;
+  const Layout L = make_layout(M, K, N);
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0 || ws_bytes < L.total)
+    return INT8MM_EWORKSPACE;
+
+  const int m = (int)M, n = (int)N, k = (int)K, ldk = (int)L.ldk;
+  hipError_t e;
+  if (K == 0) {
+    // Empty contraction: C = 0, no outlier columns, Y = 0.
+    // (fill kernels, not hipMemsetAsync: safe inside a captured graph)
+    if (out.n_outliers) {
+      if ((e = i8mm::launch_zero_half(reinterpret_cast<uint16_t*>(out.n_outliers), 2, s)) != hipSuccess)
+        return hip_fail(e);
+    }
+    if (out.x_scale) {
+      if ((e = i8mm::launch_zero_half(reinterpret_cast<uint16_t*>(out.x_scale), 2 * M, s)) != hipSuccess)
+        return hip_fail(e);
+    }
+    if (out.C) {
+      if ((e = i8mm::launch_zero_half(reinterpret_cast<uint16_t*>(out.C), 2 * M * N, s)) != hipSuccess)
+        return hip_fail(e);
+    } else if (out.Y) {
+      if ((e = i8mm::launch_zero_half(out.Y, M * N, s)) != hipSuccess) return hip_fail(e);
+    }
+    return INT8MM_OK;
+  }
+
+  uint32_t* bits = at<uint32_t>(ws, L.bits);
+  int32_t* count = out.n_outliers ? out.n_outliers : at<int32_t>(ws, L.count);
+  float* xs = out.x_scale ? out.x_scale : at<float>(ws, L.xscale);
+  int8_t* xq = out.Xq ? out.Xq : at<int8_t>(ws, L.xq);
+  uint16_t* xo = out.X_O ? out.X_O : (L.decode ? nullptr : at<uint16_t>(ws, L.xo));
+  uint16_t* wo = out.W_O ? out.W_O : (L.decode ? nullptr : at<uint16_t>(ws, L.wo));
+
+  if (L.decode) {
+    if ((e = i8mm::launch_colmask(X, nullptr, 0, m, k, ldk, threshold, out.mask, bits, s)) != hipSuccess)
+      return hip_fail(e);
+  } else {
+    uint16_t* part = at<uint16_t>(ws, L.part);
+    if ((e = i8mm::launch_colmax_partial(X, m, k, ldk, part, s)) != hipSuccess) return hip_fail(e);
+    if ((e = i8mm::launch_colmask(X, part, L.rc, m, k, ldk, threshold, out.mask, bits, s)) != hipSuccess)
+      return hip_fail(e);
+  }
+  if ((e = i8mm::launch_quant_rows(X, m, k, ldk, bits, xq, xs, xo, count, out.outlier_idx, Wq,
+                                   w_scale, n, wo, s)) != hipSuccess)
+    return hip_fail(e);
+
+  uint16_t* Y = out.C ? nullptr : out.Y;
+  if (out.C == nullptr && Y == nullptr) return INT8MM_OK;
+  if (ev_start != nullptr && (e = hipEventRecord(ev_start, s)) != hipSuccess) return hip_fail(e);
+  if (L.decode)
+    e = i8mm::launch_gemm_decode(xq, Wq, m, n, k, ldk, xs, w_scale, X, bits, Y, out.C, s);
+  else
+    e = i8mm::launch_gemm_prefill(xq, Wq, m, n, ldk, xs, w_scale, xo, wo, count, Y, out.C, s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ev_stop != nullptr && (e = hipEventRecord(ev_stop, s)) != hipSuccess) return hip_fail(e);
+  return INT8MM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+INT8MM_API int64_t int8_weight_ld(int64_t K) { return K < 0 ? -1 : ld_of(K); }
+
+INT8MM_API int int8_prepare_weight(const int8mm_half* W, int64_t N, int64_t K, int8_t* Wq, float* w_scale,
+                        hipStream_t stream) {
+  if (N < 0 || K < 0 || K > INT8MM_MAX_K || N > kMaxRows) return INT8MM_ESHAPE;
+  if (N == 0) return INT8MM_OK;
+  if (w_scale == nullptr || (K > 0 && (W == nullptr || Wq == nullptr))) return INT8MM_EINVAL;
+  hipError_t e = i8mm::launch_prepare_weight(W, (int)N, (int)K, (int)ld_of(K), Wq, w_scale, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return INT8MM_OK;
+}
+
+INT8MM_API size_t int8_matmul_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (check_shape(M, K, N) != INT8MM_OK) return 0;
+  return make_layout(M, K, N).total;
+}
+
+INT8MM_API int int8_matmul(const int8mm_half* X, int64_t M, int64_t K, const int8_t* Wq,
+                const float* w_scale, int64_t N, float threshold, int8mm_half* Y,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Outputs out;
+  out.Y = Y;
+  return run(X, M, K, Wq, w_scale, N, threshold, out, false, workspace, workspace_bytes, stream);
+}
+
+INT8MM_API int int8_matmul_profiled(const int8mm_half* X, int64_t M, int64_t K, const int8_t* Wq,
+                                    const float* w_scale, int64_t N, float threshold,
+                                    int8mm_half* Y, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream, hipEvent_t matmul_start,
+                                    hipEvent_t matmul_stop) {
+  Outputs out;
+  out.Y = Y;
+  return run(X, M, K, Wq, w_scale, N, threshold, out, false, workspace, workspace_bytes, stream,
+             matmul_start, matmul_stop);
+}
+
+INT8MM_API int int8_matmul_stages(const int8mm_half* X, int64_t M, int64_t K, const int8_t* Wq,
+                       const float* w_scale, int64_t N, float threshold, uint8_t* mask,
+                       int32_t* n_outliers, int32_t* outlier_idx, int8_t* Xq, float* x_scale,
+                       int8mm_half* X_O, int8mm_half* W_O, int32_t* C, int8mm_half* Y,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Outputs out;
+  out.mask = mask;
+  out.n_outliers = n_outliers;
+  out.outlier_idx = outlier_idx;
+  out.Xq = Xq;
+  out.x_scale = x_scale;
+  out.X_O = X_O;
+  out.W_O = W_O;
+  out.C = C;
+  out.Y = Y;
+  return run(X, M, K, Wq, w_scale, N, threshold, out, true, workspace, workspace_bytes, stream);
+}
+
+INT8MM_API const char* int8mm_strerror(int status) {
+  switch (status) {
+    case INT8MM_OK: return "ok";
+    case INT8MM_EINVAL: return "invalid argument (null pointer or bad threshold)";
+    case INT8MM_ESHAPE: return "invalid shape (negative dimension or K above the int32 bound)";
+    case INT8MM_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case INT8MM_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+INT8MM_API const char* int8mm_last_hip_error(void) { return g_hip_error; }
+
+}  // extern "C"

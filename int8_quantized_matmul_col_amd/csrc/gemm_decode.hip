@@ -1,0 +1,206 @@
+// Decode-shaped (M <= 16 rows) decomposed int8 matmul: one streaming pass
+// over the int8 weight, which is what bounds it (HBM), with the outlier
+// columns handled inline so that Wq is read exactly once per call.
+//
+// Work split: a workgroup owns G groups of 16 weight rows (output columns n)
+// and 8 waves split K between them.  Per 64-byte K step a wave loads one
+// 16-byte Xq fragment (rows m = lane%16, zero for m >= M) and G 16-byte Wq
+// fragments and issues G v_mfma_i32_16x16x64_i8.  When the 64-column window
+// holds an outlier column (wave-uniform test on the mask bits), the wave
+// also builds fp16 fragments of X_O (X values of the outlier columns, 0
+// elsewhere) and of W_O = fp16(fp32(Wq*a_w)/127) from the int8 bytes already
+// in registers, and accumulates them with v_mfma_f32_16x16x32_f16 into
+// separate fp32 accumulators ("LLM.int8() notes", section 2.3: FP16 outlier
+// term; "PyTorch 2.9 supports LLM.int8()", section 3: merged at the end).
+// The 8 per-wave partials are summed in LDS in a fixed order (deterministic)
+// and the epilogue writes Y = fp16(fp32(C)*a_x*a_w/127^2 + Y_O).
+#include "device_common.h"
+#include "launch.h"
+
+namespace i8mm {
+
+namespace {
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxWords = (133144 + 63) / 64 * 2;  // mask words for the largest K
+}  // namespace
+
+template <int G, int MODE>  // MODE 0: Y, 1: int32 C
+__global__ __launch_bounds__(kThreads) void k_gemm_decode(
+    const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K, int ldk,
+    const float* __restrict__ x_scale, const float* __restrict__ w_scale,
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ mask_bits,
+    uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
+  __shared__ uint32_t s_bits[kMaxWords];
+  __shared__ int s_red[kWaves][G * 256];
+  __shared__ int s_any;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int nw = ldk / 32;
+  if (t == 0) s_any = 0;
+  __syncthreads();
+  {
+    uint32_t any = 0;
+    for (int w = t; w < nw; w += kThreads) {
+      const uint32_t b = mask_bits[w];
+      s_bits[w] = b;
+      any |= b;
+    }
+    if (any) s_any = 1;  // benign race: every writer stores 1
+  }
+  __syncthreads();
+  const bool has_outliers = s_any != 0;
+
+  const int n_base = blockIdx.x * (G * 16);
+  const int nsteps = ldk / 64;
+  const int s0 = (nsteps * wave) / kWaves, s1 = (nsteps * (wave + 1)) / kWaves;
+  const int ml = lane & 15;   // row of the Xq fragment / column of the result
+  const int kq = (lane >> 4) * 16;  // byte offset of this lane inside the 64-byte step
+
+  const int8_t* xrow = Xq + (size_t)min(ml, M - 1) * ldk + kq;
+  const bool xvalid = ml < M;
+  const int8_t* wrow[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) wrow[g] = Wq + (size_t)min(n_base + g * 16 + ml, N - 1) * ldk + kq;
+
+  v4i acc[G];
+  v4f acco[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    acc[g] = v4i{};
+    acco[g] = v4f{};
+  }
+
+  for (int s = s0; s < s1; ++s) {
+    const size_t off = (size_t)s * 64;
+    v4i b[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) b[g] = *reinterpret_cast<const v4i*>(wrow[g] + off);
+    v4i a = xvalid ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[g], acc[g], 0, 0, 0);
+
+    if (has_outliers && (s_bits[2 * s] | s_bits[2 * s + 1])) {
+      // fp16 outlier fragments for this lane's 16 columns k0 .. k0+15
+      const int k0 = s * 64 + kq;
+      const uint32_t ob = (s_bits[k0 >> 5] >> (k0 & 31)) & 0xffffu;
+      v8h xa[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        uint16_t v = 0;
+        if (((ob >> e) & 1u) && xvalid) v = X[(size_t)ml * K + k0 + e];
+        xa[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int n = min(n_base + g * 16 + ml, N - 1);
+        const float aw = w_scale[n];
+        v8h wb[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          uint16_t v = 0;
+          if ((ob >> e) & 1u) {
+            const int q = (int)(int8_t)((b[g][e >> 2] >> ((e & 3) * 8)) & 0xff);
+            v = dequant_w_half(q, aw);
+          }
+          wb[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
+        }
+        acco[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], wb[0], acco[g], 0, 0, 0);
+        acco[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], wb[1], acco[g], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- fixed-order reduction of the 8 wave partials.  Element e = g*256 +
+  // lane*4 + r of a wave holds result row m = 4*(lane/16) + r, column
+  // n = n_base + 16*g + lane%16 (16x16 MFMA accumulator layout).
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_red[wave][g * 256 + lane * 4 + r] = acc[g][r];
+  __syncthreads();
+  int csum[(G * 256 + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int u = 0; u < (G * 256 + kThreads - 1) / kThreads; ++u) {
+    const int e = t + u * kThreads;
+    int v = 0;
+    if (e < G * 256) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += s_red[w][e];
+    }
+    csum[u] = v;
+  }
+  float osum[(G * 256 + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int u = 0; u < (G * 256 + kThreads - 1) / kThreads; ++u) osum[u] = 0.0f;
+  if (MODE == 0 && has_outliers) {
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_red[wave][g * 256 + lane * 4 + r] = __float_as_int(acco[g][r]);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < (G * 256 + kThreads - 1) / kThreads; ++u) {
+      const int e = t + u * kThreads;
+      float v = 0.0f;
+      if (e < G * 256) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v += __int_as_float(s_red[w][e]);
+      }
+      osum[u] = v;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < (G * 256 + kThreads - 1) / kThreads; ++u) {
+    const int e = t + u * kThreads;
+    if (e >= G * 256) continue;
+    const int g = e >> 8, ln = (e >> 2) & 63, r = e & 3;
+    const int m = (ln >> 4) * 4 + r;
+    const int n = n_base + g * 16 + (ln & 15);
+    if (m >= M || n >= N) continue;
+    if (MODE == 1) {
+      C[(size_t)m * N + n] = csum[u];
+    } else {
+      const float sc = x_scale[m] * w_scale[n] * kInv127Sq;
+      Y[(size_t)m * N + n] = f2h((float)csum[u] * sc + osum[u]);
+    }
+  }
+}
+
+template <int G>
+static void launch_g(dim3 grid, hipStream_t s, const int8_t* Xq, const int8_t* Wq, int M, int N,
+                     int K, int ldk, const float* xs, const float* ws, const uint16_t* X,
+                     const uint32_t* mb, uint16_t* Y, int32_t* C) {
+  if (C != nullptr)
+    hipLaunchKernelGGL((k_gemm_decode<G, 1>), grid, dim3(kThreads), 0, s, Xq, Wq, M, N, K, ldk,
+                       xs, ws, X, mb, Y, C);
+  else
+    hipLaunchKernelGGL((k_gemm_decode<G, 0>), grid, dim3(kThreads), 0, s, Xq, Wq, M, N, K, ldk,
+                       xs, ws, X, mb, Y, C);
+}
+
+hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
+                              const float* x_scale, const float* w_scale, const uint16_t* X,
+                              const uint32_t* mask_bits, uint16_t* Y, int32_t* C, hipStream_t s) {
+  // Spread the 16-row groups evenly over the 256 CUs: G groups per workgroup.
+  const int groups = (N + 15) / 16;
+  int G = (groups + 255) / 256;
+  if (G > 8) G = 8;
+  if (G < 1) G = 1;
+  dim3 grid((groups + G - 1) / G);
+  switch (G) {
+    case 1: launch_g<1>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 2: launch_g<2>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 3: launch_g<3>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 4: launch_g<4>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 5: launch_g<5>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 6: launch_g<6>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 7: launch_g<7>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    default: launch_g<8>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace i8mm

@@ -1,0 +1,44 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the
+// public C ABI is include/int8mm.h).  Each returns the HIP status of its
+// launch.  Shapes are validated by the caller (api.hip) before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8mm {
+
+// Rows of X reduced by one block of the column-absmax pass (prefill path).
+constexpr int kColmaxRowsPerChunk = 256;
+
+hipError_t launch_prepare_weight(const uint16_t* W, int N, int K, int ldk, int8_t* Wq,
+                                 float* w_scale, hipStream_t s);
+
+// Prefill: per-chunk column absmax partials part[rc][ldk] (u16 |x| bits).
+hipError_t launch_colmax_partial(const uint16_t* X, int M, int K, int ldk, uint16_t* part,
+                                 hipStream_t s);
+// Reduces the partials (rc > 0) or scans X directly (part == nullptr, small
+// M) into the outlier mask: bytes mask8[K] (optional) and bits mask_bits[ldk/32].
+hipError_t launch_colmask(const uint16_t* X, const uint16_t* part, int rc, int M, int K,
+                          int ldk, float threshold, uint8_t* mask8, uint32_t* mask_bits,
+                          hipStream_t s);
+// Row quantization over R, outlier compaction, |O| and the O list; optionally
+// the dequantized outlier weight rows W_O (when WO != nullptr).
+hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uint32_t* mask_bits,
+                             int8_t* Xq, float* x_scale, uint16_t* XO, int32_t* n_out,
+                             int32_t* out_idx, const int8_t* Wq, const float* w_scale, int N,
+                             uint16_t* WO, hipStream_t s);
+// Prefill tile GEMM: int8 MFMA over K, then fp16 MFMA over the outlier slice,
+// fused dequant epilogue (Y), or int32 accumulators only (C).
+hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int ldk,
+                               const float* x_scale, const float* w_scale, const uint16_t* XO,
+                               const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
+                               hipStream_t s);
+// Decode (M <= 16): one streaming pass over Wq, outliers handled inline.
+hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
+                              const float* x_scale, const float* w_scale, const uint16_t* X,
+                              const uint32_t* mask_bits, uint16_t* Y, int32_t* C, hipStream_t s);
+// Y[0 .. count) = 0 (K == 0 case).
+hipError_t launch_zero_half(uint16_t* Y, int64_t count, hipStream_t s);
+
+}  // namespace i8mm

@@ -1,0 +1,158 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every entry point include/int8mm.h declares,
+and reject bad arguments on the host with the documented status codes
+before anything is enqueued.  Fake non-null device addresses are used where
+a pointer must be non-null; every call here fails validation (or is an
+empty no-op) before any pointer is touched.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import int8_quantized_matmul_col_amd as mm
+from int8_quantized_matmul_col_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "int8mm.h")
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+FAKE_WS = 0x7F0000100000  # 256-byte aligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from int8_quantized_matmul_col_amd import build
+        build.build()
+    return mm.load()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"INT8MM_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    assert fns == sorted(["int8_weight_ld", "int8_prepare_weight", "int8_matmul_workspace_size",
+                          "int8_matmul", "int8_matmul_stages", "int8_matmul_profiled", "int8mm_strerror",
+                          "int8mm_last_hip_error"])
+    assert set(fns) == set(binding.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    consts = dict(re.findall(r"#define (INT8MM_\w+) \(?(-?\d+)\)?", src))
+    assert int(consts["INT8MM_OK"]) == binding.INT8MM_OK
+    assert int(consts["INT8MM_EINVAL"]) == binding.INT8MM_EINVAL
+    assert int(consts["INT8MM_ESHAPE"]) == binding.INT8MM_ESHAPE
+    assert int(consts["INT8MM_EWORKSPACE"]) == binding.INT8MM_EWORKSPACE
+    assert int(consts["INT8MM_EHIP"]) == binding.INT8MM_EHIP
+    assert int(consts["INT8MM_MAX_K"]) == binding.INT8MM_MAX_K
+    assert int(consts["INT8MM_DECODE_MAX_M"]) == binding.INT8MM_DECODE_MAX_M
+
+
+def test_int32_accumulator_bound():
+    # 127^2 * K must fit in int32 exactly up to MAX_K
+    assert 127 * 127 * binding.INT8MM_MAX_K < 2 ** 31
+    assert 127 * 127 * (binding.INT8MM_MAX_K + 1) >= 2 ** 31
+
+
+def test_weight_ld(lib):
+    assert lib.int8_weight_ld(-1) == -1
+    for K, ld in [(0, 0), (1, 64), (63, 64), (64, 64), (65, 128), (4096, 4096), (11008, 11008),
+                  (133144, 133184)]:
+        assert lib.int8_weight_ld(K) == ld
+
+
+def test_workspace_size(lib):
+    ws = lib.int8_matmul_workspace_size
+    assert ws(-1, 8, 8) == 0 and ws(8, -1, 8) == 0 and ws(8, 8, -1) == 0
+    assert ws(8, binding.INT8MM_MAX_K + 1, 8) == 0
+    assert ws(8, binding.INT8MM_MAX_K, 8) > 0
+    assert ws(0, 0, 0) >= 256
+    assert ws(4096, 4096, 4096) % 256 == 0
+    # grows with every dimension; holds at least Xq (M*ldk) and, on the
+    # prefill path, the worst-case X_O and W_O slices
+    assert ws(4096, 4096, 4096) >= 4096 * 4096 * (1 + 2) + 4096 * 4096 * 2
+    assert ws(4096, 8192, 4096) > ws(4096, 4096, 4096)
+    assert ws(16, 8192, 28672) < ws(17, 8192, 28672)  # decode path needs no W_O copy
+
+
+def _mm(lib, X=FAKE, M=4, K=8, Wq=FAKE, s=FAKE, N=4, t=6.0, Y=FAKE, ws=FAKE_WS, nbytes=1 << 30):
+    return lib.int8_matmul(X, M, K, Wq, s, N, t, Y, ws, nbytes, None)
+
+
+def test_matmul_rejects_bad_arguments(lib):
+    assert _mm(lib, M=-1) == binding.INT8MM_ESHAPE
+    assert _mm(lib, K=-1) == binding.INT8MM_ESHAPE
+    assert _mm(lib, N=-1) == binding.INT8MM_ESHAPE
+    assert _mm(lib, K=binding.INT8MM_MAX_K + 1) == binding.INT8MM_ESHAPE
+    assert _mm(lib, t=float("nan")) == binding.INT8MM_EINVAL
+    assert _mm(lib, t=-0.5) == binding.INT8MM_EINVAL
+    assert _mm(lib, X=None) == binding.INT8MM_EINVAL
+    assert _mm(lib, Wq=None) == binding.INT8MM_EINVAL
+    assert _mm(lib, s=None) == binding.INT8MM_EINVAL
+    assert _mm(lib, Y=None) == binding.INT8MM_EINVAL
+    assert _mm(lib, ws=None) == binding.INT8MM_EWORKSPACE
+    assert _mm(lib, ws=FAKE_WS + 16) == binding.INT8MM_EWORKSPACE
+    need = lib.int8_matmul_workspace_size(4, 8, 4)
+    assert _mm(lib, nbytes=need - 1) == binding.INT8MM_EWORKSPACE
+
+
+def test_matmul_empty_is_a_noop(lib):
+    # nothing to compute: returns OK without touching any pointer
+    assert _mm(lib, M=0, X=FAKE, Y=FAKE) == binding.INT8MM_OK
+    assert _mm(lib, N=0) == binding.INT8MM_OK
+    assert _mm(lib, M=0, N=0, K=0) == binding.INT8MM_OK
+
+
+def test_matmul_accepts_infinite_threshold_in_validation(lib):
+    # +inf passes the threshold check: the call then fails on the workspace
+    assert _mm(lib, t=math.inf, ws=None) == binding.INT8MM_EWORKSPACE
+
+
+def test_stages_rejects_bad_arguments(lib):
+    f = lib.int8_matmul_stages
+    args = lambda **kw: [kw.get("X", FAKE), kw.get("M", 4), kw.get("K", 8), FAKE, FAKE,
+                         kw.get("N", 4), kw.get("t", 6.0)] + [None] * 9 + \
+                        [kw.get("ws", FAKE_WS), kw.get("nbytes", 1 << 30), None]
+    assert f(*args(M=-3)) == binding.INT8MM_ESHAPE
+    assert f(*args(t=float("nan"))) == binding.INT8MM_EINVAL
+    assert f(*args(X=None)) == binding.INT8MM_EINVAL
+    assert f(*args(ws=None)) == binding.INT8MM_EWORKSPACE
+    assert f(*args(M=0)) == binding.INT8MM_OK
+
+
+def test_prepare_weight_rejects_bad_arguments(lib):
+    f = lib.int8_prepare_weight
+    assert f(FAKE, -1, 8, FAKE, FAKE, None) == binding.INT8MM_ESHAPE
+    assert f(FAKE, 4, -1, FAKE, FAKE, None) == binding.INT8MM_ESHAPE
+    assert f(FAKE, 4, binding.INT8MM_MAX_K + 1, FAKE, FAKE, None) == binding.INT8MM_ESHAPE
+    assert f(None, 4, 8, FAKE, FAKE, None) == binding.INT8MM_EINVAL
+    assert f(FAKE, 4, 8, None, FAKE, None) == binding.INT8MM_EINVAL
+    assert f(FAKE, 4, 8, FAKE, None, None) == binding.INT8MM_EINVAL
+    assert f(FAKE, 0, 8, FAKE, FAKE, None) == binding.INT8MM_OK  # empty weight
+
+
+def test_strerror(lib):
+    for st in (0, -1, -2, -3, -4):
+        assert lib.int8mm_strerror(st)
+    assert lib.int8mm_strerror(12345) == b"unknown status"
+    assert lib.int8mm_last_hip_error() == b""
+
+
+def test_binding_raises_on_status(lib):
+    with pytest.raises(binding.Int8mmError) as e:
+        binding._check("int8_matmul", binding.INT8MM_ESHAPE)
+    assert "invalid shape" in str(e.value)

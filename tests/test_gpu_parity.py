@@ -1,0 +1,153 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle,
+element by element, on seeded inputs at sizes the oracle finishes in
+seconds: several tiles, ragged tails, both kernels (decode M <= 16 and the
+prefill tile GEMM), and the method's degenerate cases."""
+
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_cases import run_case, check_prepare, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(M, K, N, seed, n_out=3, lo=8.0, hi=60.0, kind="uniform", wstd=0.02):
+    X, _ = workloads.make_x(M, K, seed, n_out, lo, hi, kind)
+    W = workloads.make_w(N, K, seed, wstd)
+    return X, W
+
+
+SHAPES = [
+    # (M, K, N, n_out, t)          decode path: M <= 16
+    (1, 64, 16, 1, 6.0),
+    (1, 1, 1, 0, 6.0),
+    (4, 1000, 300, 2, 6.0),
+    (16, 1024, 1024, 2, 6.0),
+    (5, 3, 7, 1, 6.0),
+    (16, 520, 100, 4, 0.0),
+    (9, 200, 33, 3, math.inf),
+    # prefill path: M > 16
+    (17, 1024, 1024, 2, 6.0),
+    (300, 520, 300, 5, 6.0),
+    (257, 257, 257, 3, 6.0),
+    (33, 37, 29, 2, 6.0),          # K % 8 != 0: unaligned rows of X
+    (512, 1024, 768, 6, 6.0),
+    (256, 4096, 256, 20, 6.0),
+    (64, 130, 40, 2, 0.0),         # every non-zero column is an outlier
+    (96, 320, 96, 4, math.inf),    # pure int8
+    (40, 96, 520, 90, 0.5),        # |O| close to K
+]
+
+
+@pytest.mark.parametrize("M,K,N,n_out,t", SHAPES)
+def test_parity_shapes(lib, M, K, N, n_out, t):
+    print(f"case M={M} K={K} N={N} n_out={n_out} t={t}", flush=True)
+    X, W = _case(M, K, N, seed=M * 7919 + K * 31 + N, n_out=n_out)
+    run_case(lib, X, W, t)
+
+
+def test_threshold_equal_to_column_max_is_not_outlier(lib):
+    X, W = _case(40, 256, 64, seed=3, n_out=0)
+    X[:, 10] = np.float16(0.5)
+    X[7, 10] = np.float16(6.0)   # column max exactly t: stays regular
+    X[3, 20] = np.float16(6.00390625)  # next fp16 above t: outlier
+    X[:, 30] = np.float16(-6.0)
+    for M in (40, 8):
+        Y, _ = run_case(lib, X[:M].copy(), W, 6.0)
+
+
+def test_zero_rows_and_columns(lib):
+    X, W = _case(48, 200, 80, seed=4, n_out=3)
+    X[5] = 0            # all-zero row: scale 0, codes 0
+    X[:, 17] = 0        # all-zero column
+    W[9] = 0            # all-zero weight channel: a_w = 0
+    run_case(lib, X, W, 6.0)
+    run_case(lib, X[:12].copy(), W, 6.0)
+    # a row whose only non-zero entries are outliers: empty R-range -> a_x = 0
+    X2 = X.copy()
+    X2[6] = 0
+    X2[6, 3] = 50.0
+    run_case(lib, X2, W, 6.0)
+
+
+def test_exact_ties_round_half_even(lib):
+    rng = np.random.default_rng(8)
+    M, K, N = 32, 128, 48
+    # rows with R-absmax 127/32 and entries odd/64: 127*x/a = 32*x is an exact .5 tie
+    X = (rng.integers(-127, 128, (M, K)) * 2 + 1).astype(np.float32) / 64.0
+    X = np.clip(X, -3.96875, 3.96875)
+    X[:, 0] = 3.96875
+    X = X.astype(np.float16)
+    W = (rng.integers(-127, 128, (N, K)) * 2 + 1).astype(np.float32) / 64.0
+    W = np.clip(W, -3.96875, 3.96875)
+    W[:, 1] = -3.96875
+    W = W.astype(np.float16)
+    for m in (M, 7):
+        run_case(lib, X[:m].copy(), W, 6.0)
+
+
+def test_heavy_tailed_sweep_small(lib):
+    X, W = _case(128, 320, 200, seed=12, n_out=8, kind="t3")
+    for t in workloads.SWEEP_THRESHOLDS:
+        run_case(lib, X, W, t)
+
+
+def test_prepare_weight_ties_and_odd_shapes(lib):
+    rng = np.random.default_rng(2)
+    W = (rng.integers(-127, 128, (37, 257)) * 2 + 1).astype(np.float32) / 64.0
+    W = np.clip(W, -3.96875, 3.96875)
+    W[:, 5] = 3.96875
+    check_prepare(lib, W.astype(np.float16))
+    check_prepare(lib, workloads.make_w(3, 1, 5))
+    check_prepare(lib, np.zeros((4, 70), np.float16))
+
+
+def test_empty_and_degenerate_shapes(lib):
+    import torch
+    mm = lib
+    W = workloads.make_w(8, 64, 1)
+    Wq, s = mm.int8_prepare_weight(to_dev(W))
+    # M == 0: empty output, no work
+    Y = mm.int8_matmul(torch.empty((0, 64), dtype=torch.float16, device="cuda"), Wq, s)
+    assert Y.shape == (0, 8)
+    # K == 0: empty contraction -> Y == 0
+    W0 = torch.empty((8, 0), dtype=torch.float16, device="cuda")
+    Wq0, s0 = mm.int8_prepare_weight(W0)
+    X0 = torch.empty((5, 0), dtype=torch.float16, device="cuda")
+    Y0 = mm.int8_matmul(X0, Wq0, s0)
+    torch.cuda.synchronize()
+    assert Y0.shape == (5, 8) and not Y0.float().abs().sum().item()
+    assert not s0.abs().sum().item()
+
+
+def test_workspace_reuse_across_shapes(lib):
+    """One workspace sized for the largest call, reused by smaller ones in a row
+    (its contents on entry must not matter)."""
+    import torch
+    mm = lib
+    ws = mm.workspace_for(300, 520, 300, "cuda")
+    ws.fill_(0xAB)
+    from oracle import int8mm_ref as ref
+    from gpu_cases import check_y
+    for (M, K, N, t) in [(300, 520, 300, 6.0), (40, 520, 300, 0.0), (3, 520, 300, 6.0),
+                         (300, 520, 300, math.inf)]:
+        X, W = _case(M, K, N, seed=M + N, n_out=4)
+        Wq, s = mm.int8_prepare_weight(to_dev(W))
+        Y = mm.int8_matmul(to_dev(X), Wq, s, threshold=t, workspace=ws)
+        torch.cuda.synchronize()
+        Wq_r, s_r = ref.prepare_weight_ref(W)
+        Y_r, st = ref.int8_matmul_ref(X, Wq_r, s_r, t, stages=True)
+        check_y(Y.cpu().numpy(), Y_r, X, Wq_r, s_r, st["O"].size)
+
+
+def test_output_overflow_gives_inf(lib):
+    # |Y| beyond the fp16 range becomes +-inf in both paths
+    M, K, N = 20, 64, 16
+    X = np.full((M, K), 100.0, np.float16)
+    W = np.full((N, K), 60.0, np.float16)
+    W[1] = -60.0
+    Y, Y_ref = run_case(lib, X, W, 1000.0)
+    assert np.isinf(Y_ref).all()

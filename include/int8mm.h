@@ -31,8 +31,15 @@
  *   - No global mutable state: calls on different streams with different
  *     workspaces may run concurrently.  Two calls that share a workspace
  *     must be ordered (e.g. on one stream).
- *   - Row-major layouts.  `ldk` below is int8_weight_ld(K): K rounded up to a
- *     multiple of 64; padding columns hold zeros.
+ *   - X and Y are row-major.  The int8 operands and the fp16 outlier slices
+ *     (the prepared weight Wq, and the stage outputs Xq, X_O, W_O) use the
+ *     library's panel-tiled layout, built for gfx950's memory path: rows are
+ *     padded to Rp = 256*ceil(R/256), each row is `row_bytes` long (ldk bytes
+ *     for int8, 2*ldk bytes for fp16, ldk = int8_weight_ld(K) = K rounded up
+ *     to 64), and byte b of row r sits at
+ *         ((r/256)*(row_bytes/64) + b/64)*16384 + (r%256)*64 + b%64,
+ *     i.e. 256-row x 64-byte blocks of 16 KiB, contiguous.  Padding columns
+ *     of Wq and Xq hold zeros.
  */
 #ifndef INT8MM_H
 #define INT8MM_H
@@ -67,9 +74,13 @@ typedef uint16_t int8mm_half;
  * (one pass over the int8 weight); larger M takes the MFMA tile GEMM. */
 #define INT8MM_DECODE_MAX_M 16
 
-/* Row stride, in elements, of every [.][ldk] buffer: K rounded up to 64.
+/* Row length, in elements, of every [.][ldk] buffer: K rounded up to 64.
  * Returns -1 for K < 0. */
 INT8MM_API int64_t int8_weight_ld(int64_t K);
+
+/* Bytes of a prepared weight: 256*ceil(N/256) * ldk.  -1 for an invalid
+ * shape. */
+INT8MM_API int64_t int8_weight_bytes(int64_t N, int64_t K);
 
 /*
  * int8_prepare_weight -- one-time per-output-channel quantization of W.
@@ -78,8 +89,9 @@ INT8MM_API int64_t int8_weight_ld(int64_t K);
  * slower" one-time quantization.)
  *
  *   W        [N][K]   float16, row-major (nn.Linear [out_features][in_features]).
- *   Wq       [N][ldk] int8 out: Wq[n][k] = clamp(rne(fp32(127*W[n][k]) / a_w[n]),
- *                     -127, 127), 0 where a_w[n] == 0; columns K..ldk-1 are 0.
+ *   Wq       int8_weight_bytes(N, K) bytes out, panel-tiled [Np][ldk]:
+ *                     Wq[n][k] = clamp(rne(fp32(127*W[n][k]) / a_w[n]), -127, 127),
+ *                     0 where a_w[n] == 0; padding rows and columns are 0.
  *   w_scale  [N]      float out: a_w[n] = max_k |W[n][k]| (the absmax itself,
  *                     not divided by 127).
  * N == 0 or K == 0 is a valid no-op (returns INT8MM_OK, nothing enqueued,
@@ -102,7 +114,8 @@ INT8MM_API size_t int8_matmul_workspace_size(int64_t M, int64_t K, int64_t N);
  * int8_matmul -- Y = decomposed int8 matmul of X with the prepared weight.
  *
  *   X         [M][K]   float16 activations (row-major, row stride K).
- *   Wq        [N][ldk] int8, w_scale [N] float: from int8_prepare_weight.
+ *   Wq        prepared weight (panel-tiled), w_scale [N] float: from
+ *                      int8_prepare_weight.
  *   threshold          outlier threshold t >= 0 (+inf allowed): column k is an
  *                      outlier when max_m |X[m][k]| > t (strict).  t = 0 sends
  *                      every non-zero column to the fp16 path; t = +inf none.
@@ -127,12 +140,15 @@ INT8MM_API int int8_matmul(const int8mm_half* X, int64_t M, int64_t K,
  *   mask        [K]      uint8 out: 1 where column k is an outlier.
  *   n_outliers  [1]      int32 out: |O|.
  *   outlier_idx [K]      int32 out: O in ascending order (first |O| valid).
- *   Xq          [M][ldk] int8 out: quantized X, 0 in outlier and pad columns.
+ *   Xq          [Mp][ldk] int8 out, panel-tiled: quantized X, 0 in outlier and
+ *                        pad columns (rows M..Mp-1 unspecified).
  *   x_scale     [M]      float out: a_x[m] = max over R of |X[m][k]| (0 if none).
- *   X_O         [M][ldk] float16 out: X_O[m][j] = X[m][O_j] for j < |O|, then
+ *   X_O         [Mp][ldk] float16 out, panel-tiled (rows of 2*ldk bytes):
+ *                        X_O[m][j] = X[m][O_j] for j < |O|, then zeros up to
+ *                        the next multiple of 64 columns (rest unspecified).
+ *   W_O         [Np][ldk] float16 out, panel-tiled: W_O[n][j] =
+ *                        fp16(fp32(Wq[n][O_j]*a_w[n])/127) for j < |O|, then
  *                        zeros up to the next multiple of 64 columns.
- *   W_O         [N][ldk] float16 out: W_O[n][j] = fp16(fp32(Wq[n][O_j]*a_w[n])/127)
- *                        for j < |O|, then zeros up to the next multiple of 64.
  *   C           [M][N]   int32 out: C[m][n] = sum_k Xq[m][k] * Wq[n][k].
  *   Y           [M][N]   float16 out.
  * Errors as int8_matmul.

@@ -21,7 +21,11 @@ from .binding import (  # noqa: F401
     int8_matmul_stages,
     int8_matmul_workspace_size,
     int8_prepare_weight,
+    int8_weight_bytes,
     int8_weight_ld,
+    padded_rows,
+    unpack_weight,
+    untile,
     load,
     workspace_for,
 )

@@ -34,6 +34,7 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 SIGNATURES = {
     "int8_weight_ld": (ctypes.c_int64, [_I64]),
+    "int8_weight_bytes": (ctypes.c_int64, [_I64, _I64]),
     "int8_prepare_weight": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "int8_matmul_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "int8_matmul": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P,
@@ -113,12 +114,43 @@ def int8_weight_ld(K: int) -> int:
     return int(load().int8_weight_ld(int(K)))
 
 
+def int8_weight_bytes(N: int, K: int) -> int:
+    """Bytes of a prepared weight (panel-tiled, rows padded to 256)."""
+    return int(load().int8_weight_bytes(int(N), int(K)))
+
+
+PANEL = 256  # rows per panel of the tiled layout
+
+
+def padded_rows(R: int) -> int:
+    return (int(R) + PANEL - 1) // PANEL * PANEL
+
+
+def untile(buf, rows: int):
+    """Row-major view of a panel-tiled [Rp][L] buffer (any dtype), first
+    `rows` rows.  Byte b of row r sits at
+    ((r/256)*(row_bytes/64) + b/64)*16384 + (r%256)*64 + b%64."""
+    import torch
+    Rp, L = buf.shape
+    row_bytes = L * buf.element_size()
+    b = buf.contiguous().view(torch.uint8).reshape(Rp // PANEL, row_bytes // 64, PANEL, 64)
+    b = b.permute(0, 2, 1, 3).reshape(Rp, row_bytes)
+    return b.view(buf.dtype)[:rows]
+
+
+def unpack_weight(Wq, N: int, K: int):
+    """Row-major int8 [N][K] copy of a prepared weight."""
+    return untile(Wq, N)[:, :K]
+
+
 def int8_matmul_workspace_size(M: int, K: int, N: int) -> int:
     return int(load().int8_matmul_workspace_size(int(M), int(K), int(N)))
 
 
 def int8_prepare_weight(W, out: Optional[Tuple] = None):
-    """W: float16 [N][K] on the GPU -> (Wq int8 [N][ldk], w_scale float32 [N])."""
+    """W: float16 [N][K] on the GPU -> (Wq, w_scale float32 [N]); Wq is the
+    panel-tiled int8 weight, stored as an int8 tensor [Np][ldk]
+    (Np = N rounded up to 256; see unpack_weight for a row-major copy)."""
     import torch
     lib = load()
     _require(W, torch.float16, "W")
@@ -127,7 +159,7 @@ def int8_prepare_weight(W, out: Optional[Tuple] = None):
     N, K = W.shape
     ldk = int8_weight_ld(K)
     if out is None:
-        Wq = torch.empty((N, ldk), dtype=torch.int8, device=W.device)
+        Wq = torch.empty((padded_rows(N), ldk), dtype=torch.int8, device=W.device)
         ws = torch.empty((N,), dtype=torch.float32, device=W.device)
     else:
         Wq, ws = out
@@ -156,8 +188,8 @@ def int8_matmul(X, Wq, w_scale, threshold: float = DEFAULT_THRESHOLD, out=None, 
     _require(w_scale, torch.float32, "w_scale", dev)
     M, Kx = X.shape
     K = Kx if K is None else K
-    N = Wq.shape[0]
-    if Kx != K or Wq.shape[1] != int8_weight_ld(K) or w_scale.numel() != N:
+    N = w_scale.numel()
+    if Kx != K or Wq.numel() != int8_weight_bytes(N, K):
         raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, "
                          f"w_scale {tuple(w_scale.shape)}")
     Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
@@ -176,7 +208,7 @@ def int8_matmul_profiled(X, Wq, w_scale, threshold: float, out, workspace, ev_st
     kernel (for timing that kernel alone).  All tensors preallocated."""
     lib = load()
     M, K = X.shape
-    N = Wq.shape[0]
+    N = w_scale.numel()
     st = lib.int8_matmul_profiled(_ptr(X), M, K, _ptr(Wq), _ptr(w_scale), N, float(threshold),
                                   _ptr(out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(),
@@ -188,7 +220,9 @@ def int8_matmul_profiled(X, Wq, w_scale, threshold: float, out, workspace, ev_st
 def int8_matmul_stages(X, Wq, w_scale, threshold: float = DEFAULT_THRESHOLD,
                        want_c: bool = True, workspace=None) -> Dict[str, object]:
     """Runs the same kernels as int8_matmul and returns every intermediate:
-    mask, n_outliers, outlier_idx, Xq, x_scale, X_O, W_O and C (want_c) or Y."""
+    mask, n_outliers, outlier_idx, Xq [M][ldk], x_scale, X_O [M][ldk],
+    W_O [N][ldk] (row-major views of the library's tiled buffers) and C
+    (want_c) or Y."""
     import torch
     lib = load()
     _require(X, torch.float16, "X")
@@ -196,18 +230,19 @@ def int8_matmul_stages(X, Wq, w_scale, threshold: float = DEFAULT_THRESHOLD,
     _require(Wq, torch.int8, "Wq", dev)
     _require(w_scale, torch.float32, "w_scale", dev)
     M, K = X.shape
-    N = Wq.shape[0]
+    N = w_scale.numel()
     ldk = int8_weight_ld(K)
-    if Wq.shape[1] != ldk or w_scale.numel() != N:
+    if Wq.numel() != int8_weight_bytes(N, K):
         raise ValueError("shape mismatch")
+    Mp, Np = padded_rows(M), padded_rows(N)
     o = dict(
         mask=torch.zeros((K,), dtype=torch.uint8, device=dev),
         n_outliers=torch.full((1,), -1, dtype=torch.int32, device=dev),
         outlier_idx=torch.full((K,), -1, dtype=torch.int32, device=dev),
-        Xq=torch.zeros((M, ldk), dtype=torch.int8, device=dev),
+        Xq=torch.zeros((Mp, ldk), dtype=torch.int8, device=dev),
         x_scale=torch.zeros((M,), dtype=torch.float32, device=dev),
-        X_O=torch.zeros((M, ldk), dtype=torch.float16, device=dev),
-        W_O=torch.zeros((N, ldk), dtype=torch.float16, device=dev),
+        X_O=torch.zeros((Mp, ldk), dtype=torch.float16, device=dev),
+        W_O=torch.zeros((Np, ldk), dtype=torch.float16, device=dev),
     )
     C = torch.zeros((M, N), dtype=torch.int32, device=dev) if want_c else None
     Y = None if want_c else torch.empty((M, N), dtype=torch.float16, device=dev)
@@ -218,6 +253,9 @@ def int8_matmul_stages(X, Wq, w_scale, threshold: float = DEFAULT_THRESHOLD,
         _ptr(o["x_scale"]), _ptr(o["X_O"]), _ptr(o["W_O"]), _ptr(C), _ptr(Y),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check("int8_matmul_stages", st)
+    o["Xq"] = untile(o["Xq"], M)
+    o["X_O"] = untile(o["X_O"], M)
+    o["W_O"] = untile(o["W_O"], N)
     if want_c:
         o["C"] = C
     else:

@@ -11,76 +11,111 @@
 //   section 2: dynamic per-input scales, no calibration), 0 in O columns.
 // * X_O[m][j] = X[m][O_j]; W_O[n][j] = fp16(fp32(Wq[n][O_j]*a_w[n])/127).
 //
-// Memory layout: the mask is kept as bits (ldk/32 words); each block of the
-// row pass rebuilds the exclusive prefix count of the mask words in LDS, so
-// a column's slot in the compacted slices is prefix[word] + popcount of the
-// lower bits -- no separate scan launch and no global O list is needed by the
-// consumers.
+// Xq, X_O and W_O are written in the panel-tiled layout of tile_layout.h.
+// The mask is kept as bits (ldk/32 words); each block of the row pass
+// rebuilds the exclusive prefix count of the mask words in LDS, so a column's
+// slot in the compacted slices is prefix[word] + popcount of the lower bits:
+// no separate scan launch and no global O list is needed by the consumers.
 #include "device_common.h"
 #include "launch.h"
+#include "tile_layout.h"
 
 namespace i8mm {
 
+namespace {
+constexpr int kColBlock = 512;  // columns per block of the column-absmax pass
+constexpr int kRowChunk = kColmaxRowsPerChunk;
+}  // namespace
+
 // ---------------------------------------------------------------- column absmax
 
-// grid ceil(ldk/256) * ceil(M/256) (column block fastest); block 256 = 32 column lanes x 8 row lanes,
-// each lane reads 8 consecutive columns (16 bytes) of every 8th row of the
-// chunk.  A wave reads 2 rows x 512 contiguous bytes per load.
+// grid = ceil(ldk/512) column blocks x ceil(M/64) row chunks (column block
+// fastest).  Block 256 = 64 column lanes x 4 row lanes; each lane reads 8
+// consecutive columns (16 bytes) of 16 rows of the chunk, all loads issued
+// before use.  A wave reads one 1 KiB row segment per load instruction.
 __global__ __launch_bounds__(256) void k_colmax_partial(const uint16_t* __restrict__ X, int M,
                                                         int K, int ldk, int vec,
                                                         uint16_t* __restrict__ part) {
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int ncb = (ldk + 255) / 256;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int ncb = (ldk + kColBlock - 1) / kColBlock;
   const int cb = blockIdx.x % ncb, rcix = blockIdx.x / ncb;
-  const int c0 = cb * 256 + tx * 8;
-  const int r0 = rcix * kColmaxRowsPerChunk;
-  const int r1 = min(M, r0 + kColmaxRowsPerChunk);
+  const int c0 = cb * kColBlock + tx * 8;
+  const int r0 = rcix * kRowChunk;
   uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (c0 < K) {
-#pragma unroll 4
-    for (int r = r0 + ty; r < r1; r += 8) {
-      uint16_t h[8];
-      load8_half(X + (size_t)r * K, c0, K, vec != 0, h);
+    uint16_t h[16][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mx[i] = max(mx[i], habs_bits(h[i]));
+    for (int u = 0; u < 16; ++u) {
+      const int r = r0 + ty + 4 * u;
+      if (r < M) {
+        load8_half(X + (size_t)r * K, c0, K, vec != 0, h[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[u][i] = 0;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx[i] = max(mx[i], habs_bits(h[u][i]));
   }
-  __shared__ uint16_t s[8][256];
+  __shared__ uint16_t s[4][kColBlock];
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[ty][tx * 8 + i] = (uint16_t)mx[i];
   __syncthreads();
-  const int t = threadIdx.x;
-  uint32_t v = 0;
-#pragma unroll
-  for (int y = 0; y < 8; ++y) v = max(v, (uint32_t)s[y][t]);
-  const int col = cb * 256 + t;
-  if (col < ldk) part[(size_t)rcix * ldk + col] = (uint16_t)v;
+  for (int c = threadIdx.x; c < kColBlock; c += 256) {
+    const uint32_t v = max(max((uint32_t)s[0][c], (uint32_t)s[1][c]),
+                           max((uint32_t)s[2][c], (uint32_t)s[3][c]));
+    const int col = cb * kColBlock + c;
+    if (col < ldk) part[(size_t)rcix * ldk + col] = (uint16_t)v;
+  }
 }
 
-// grid ceil(ldk/256), one thread per column.  Reduces the rc partials (or, when
-// part == nullptr, the M rows of X directly) and compares with the threshold.
-// Each wave covers 64 consecutive columns and writes two mask words.
+// grid ceil(ldk/64); block 256 = 64 columns x 4 partial lanes.  Reduces the rc
+// partials (or, when part == nullptr, the M rows of X directly), compares
+// with the threshold and writes the mask bytes (optional) and bit words.
 __global__ __launch_bounds__(256) void k_colmask(const uint16_t* __restrict__ X,
                                                  const uint16_t* __restrict__ part, int rc,
                                                  int M, int K, int ldk, float threshold,
                                                  uint8_t* __restrict__ mask8,
                                                  uint32_t* __restrict__ mask_bits) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
+  const int cl = threadIdx.x & 63, pl = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + cl;
   uint32_t v = 0;
   if (col < K) {
-    if (part != nullptr) {
-      for (int r = 0; r < rc; ++r) v = max(v, (uint32_t)part[(size_t)r * ldk + col]);
-    } else {
-      for (int m = 0; m < M; ++m) v = max(v, habs_bits(X[(size_t)m * K + col]));
+    const int n = part != nullptr ? rc : M;
+    int r = pl;
+    for (; r + 12 < n; r += 16) {
+      uint32_t a0, a1, a2, a3;
+      if (part != nullptr) {
+        a0 = part[(size_t)r * ldk + col];
+        a1 = part[(size_t)(r + 4) * ldk + col];
+        a2 = part[(size_t)(r + 8) * ldk + col];
+        a3 = part[(size_t)(r + 12) * ldk + col];
+      } else {
+        a0 = habs_bits(X[(size_t)r * K + col]);
+        a1 = habs_bits(X[(size_t)(r + 4) * K + col]);
+        a2 = habs_bits(X[(size_t)(r + 8) * K + col]);
+        a3 = habs_bits(X[(size_t)(r + 12) * K + col]);
+      }
+      v = max(v, max(max(a0, a1), max(a2, a3)));
     }
+    for (; r < n; r += 4)
+      v = max(v, part != nullptr ? (uint32_t)part[(size_t)r * ldk + col]
+                                 : habs_bits(X[(size_t)r * K + col]));
   }
-  const bool o = (col < K) && (h2f((uint16_t)v) > threshold);
-  if (mask8 != nullptr && col < K) mask8[col] = o ? 1 : 0;
-  const uint64_t b = __ballot(o);
-  const int wave_col0 = col & ~63;
-  if ((threadIdx.x & 63) == 0 && wave_col0 < ldk) {
-    mask_bits[wave_col0 / 32] = (uint32_t)b;
-    mask_bits[wave_col0 / 32 + 1] = (uint32_t)(b >> 32);
+  __shared__ uint32_t s[4][64];
+  s[pl][cl] = v;
+  __syncthreads();
+  if (pl == 0) {
+    v = max(max(s[0][cl], s[1][cl]), max(s[2][cl], s[3][cl]));
+    const bool o = (col < K) && (h2f((uint16_t)v) > threshold);
+    if (mask8 != nullptr && col < K) mask8[col] = o ? 1 : 0;
+    const uint64_t b = __ballot(o);
+    if (cl == 0 && blockIdx.x * 64 < ldk) {
+      mask_bits[blockIdx.x * 2] = (uint32_t)b;
+      mask_bits[blockIdx.x * 2 + 1] = (uint32_t)(b >> 32);
+    }
   }
 }
 
@@ -100,7 +135,6 @@ __device__ int load_mask_prefix(const uint32_t* __restrict__ mask_bits, int nw,
     s_bits[w] = b;
     local += __popc(b);
   }
-  // inclusive scan of `local` across the block
   int incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -138,24 +172,65 @@ __device__ __forceinline__ int select_outlier(const uint32_t* s_bits, const int*
   return lo * 32 + __ffs(b) - 1;
 }
 
-// grid = row blocks (rpb rows each, one wave per row) followed by W_O blocks
-// (64 weight rows each; only when WO != nullptr).  XO may be nullptr (the
-// decode path reads outlier values straight from X).  Dynamic LDS: 2*nw words.
+namespace {
+
+// Quantize, store and compact one 8-column chunk c of row m (the chunk's mask
+// bits are `word >> sh`).
+__device__ __forceinline__ void emit_chunk(const uint16_t h[8], int m, int c, uint32_t word, int sh,
+                                           int pre, float a, int ldk, int8_t* __restrict__ Xq,
+                                           uint16_t* __restrict__ XO) {
+  const uint32_t ob = (word >> sh) & 0xffu;
+  int q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int v = quant_code(h2f(h[i]), a);  // computed for every column, then selected
+    q[i] = ((ob >> i) & 1u) ? 0 : v;
+  }
+  uint2 out;
+  out.x = (uint32_t)pack4_i8(q[0], q[1], q[2], q[3]);
+  out.y = (uint32_t)pack4_i8(q[4], q[5], q[6], q[7]);
+  *reinterpret_cast<uint2*>(Xq + tiled_offset(m, (size_t)c * 8, ldk)) = out;
+  if (ob && XO != nullptr) {
+    int slot = pre + __popc(word & ((1u << sh) - 1u));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((ob >> i) & 1u) {
+        XO[tiled_offset(m, (size_t)slot * 2, (size_t)ldk * 2) / 2] = h[i];
+        ++slot;
+      }
+  }
+}
+
+}  // namespace
+
+// Row pass.  grid = W_O blocks (16 weight rows each; only when WO !=
+// nullptr) followed by row blocks, so the small gather work overlaps the row
+// work instead of forming a tail.  WPR = waves per row: 1 (a wave per row, 4
+// rows per block) or 4 (the whole block on one row, for few rows).  CPL =
+// 8-column chunks per lane held in registers between the absmax and the
+// quantize passes (0: re-read the row from L1/L2 instead, for long rows).
+// Dynamic LDS: 2*nw words plus the O list (up to kOListCap entries).
+constexpr int kOListCap = 4096;
+constexpr int kWoRows = 16;
+
+template <int WPR, int CPL>
 __global__ __launch_bounds__(256) void k_quant_rows(
-    const uint16_t* __restrict__ X, int M, int K, int ldk, int vec, int rpb, int n_row_blocks,
+    const uint16_t* __restrict__ X, int M, int K, int ldk, int vec, int n_wo_blocks,
     const uint32_t* __restrict__ mask_bits, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
     uint16_t* __restrict__ XO, int32_t* __restrict__ n_out, int32_t* __restrict__ out_idx,
     const int8_t* __restrict__ Wq, const float* __restrict__ w_scale, int N,
     uint16_t* __restrict__ WO) {
   extern __shared__ uint32_t s_dyn[];
+  __shared__ uint32_t s_red[4];
   const int nw = ldk / 32;
   uint32_t* s_bits = s_dyn;
   int* s_pre = reinterpret_cast<int*>(s_dyn + nw);
   const int total = load_mask_prefix(mask_bits, nw, s_bits, s_pre);
   const int opad = (total + 63) & ~63;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int rb = (int)blockIdx.x - n_wo_blocks;  // row block index (< 0: a W_O block)
 
-  if (blockIdx.x == 0) {
+  if (rb == 0) {
     if (t == 0 && n_out != nullptr) *n_out = total;
     if (out_idx != nullptr) {
       for (int w = t; w < nw; w += 256) {
@@ -169,64 +244,116 @@ __global__ __launch_bounds__(256) void k_quant_rows(
     }
   }
 
-  if ((int)blockIdx.x < n_row_blocks) {
-    const int nch = ldk / 8;
-    const int m_end = min(M, ((int)blockIdx.x + 1) * rpb);
-    for (int m = blockIdx.x * rpb + wave; m < m_end; m += 4) {
-      const uint16_t* row = X + (size_t)m * K;
-      uint32_t mx = 0;
-      for (int c = lane; c < nch; c += 64) {
-        uint16_t h[8];
-        load8_half(row, c * 8, K, vec != 0, h);
-        const uint32_t ob = (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (!((ob >> i) & 1u)) mx = max(mx, habs_bits(h[i]));
-      }
-      mx = wave_max(mx);
-      const float a = h2f((uint16_t)mx);
-      int8_t* qrow = Xq + (size_t)m * ldk;
-      uint16_t* orow = XO != nullptr ? XO + (size_t)m * ldk : nullptr;
-      for (int c = lane; c < nch; c += 64) {
-        uint16_t h[8];
-        load8_half(row, c * 8, K, vec != 0, h);
-        const uint32_t word = s_bits[c >> 2];
-        const int sh = (c & 3) * 8;
-        const uint32_t ob = (word >> sh) & 0xffu;
-        int q[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = ((ob >> i) & 1u) ? 0 : quant_code(h2f(h[i]), a);
-        uint2 out;
-        out.x = (uint32_t)pack4_i8(q[0], q[1], q[2], q[3]);
-        out.y = (uint32_t)pack4_i8(q[4], q[5], q[6], q[7]);
-        *reinterpret_cast<uint2*>(qrow + c * 8) = out;
-        if (ob && orow != nullptr) {
-          const int base = s_pre[c >> 2] + __popc(word & ((1u << sh) - 1u));
-          int r = 0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if ((ob >> i) & 1u) orow[base + r++] = h[i];
+  if (rb < 0) {
+    // ---- W_O[n][j] for 16 weight rows: the O list in LDS (when it fits),
+    // then one (row, j) item per thread and pass, loads issued together.
+    int* s_olist = reinterpret_cast<int*>(s_dyn + 2 * nw);
+    const bool in_lds = total <= kOListCap;
+    if (in_lds) {
+      for (int w = t; w < nw; w += 256) {
+        uint32_t b = s_bits[w];
+        int slot = s_pre[w];
+        while (b) {
+          s_olist[slot++] = w * 32 + __ffs(b) - 1;
+          b &= b - 1;
         }
       }
-      if (orow != nullptr)
-        for (int j = total + lane; j < opad; j += 64) orow[j] = 0;
-      if (lane == 0) x_scale[m] = a;
     }
-  } else if (WO != nullptr) {
-    const int n0 = ((int)blockIdx.x - n_row_blocks) * 64;
-    const int items = 64 * opad;
-    for (int idx = t; idx < items; idx += 256) {
-      const int nl = idx / opad;
-      const int j = idx - nl * opad;
-      const int n = n0 + nl;
-      if (n >= N) break;  // idx grows with nl: every later item is past N too
-      uint16_t v = 0;
-      if (j < total) {
-        const int k = select_outlier(s_bits, s_pre, nw, j);
-        v = dequant_w_half((int)Wq[(size_t)n * ldk + k], w_scale[n]);
+    __syncthreads();
+    const int n0 = blockIdx.x * kWoRows;
+    const int nl = t >> 4, jl = t & 15;
+    const int n = n0 + nl;
+    if (n < N) {
+      const float aw = w_scale[n];
+      for (int j0 = 0; j0 < opad; j0 += 64) {
+        int q[4];
+        bool live[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 + u * 16 + jl;
+          live[u] = j < total;
+          q[u] = 0;
+          if (live[u]) {
+            const int k = in_lds ? s_olist[j] : select_outlier(s_bits, s_pre, nw, j);
+            q[u] = (int)Wq[tiled_offset(n, (size_t)k, ldk)];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 + u * 16 + jl;
+          WO[tiled_offset(n, (size_t)j * 2, (size_t)ldk * 2) / 2] =
+              live[u] ? dequant_w_half(q[u], aw) : (uint16_t)0;
+        }
       }
-      WO[(size_t)n * ldk + j] = v;
     }
+    return;
+  }
+
+  // ---- rows
+  constexpr int RPB = 4 / WPR;               // rows per block
+  constexpr int LPR = 64 * WPR;              // lanes per row
+  const int m = rb * RPB + wave / WPR;
+  const int rl = (wave % WPR) * 64 + lane;   // lane index within the row
+  const int nch = ldk / 8;
+  const bool active = m < M;
+  const uint16_t* row = X + (size_t)min(m, M - 1) * K;
+  uint16_t h[CPL > 0 ? CPL : 1][8];
+  uint32_t mx = 0;
+  if (CPL > 0) {
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = rl + u * LPR;
+      if (c < nch) {
+        load8_half(row, c * 8, K, vec != 0, h[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[u][i] = 0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int c = rl + u * LPR;
+      const uint32_t ob = c < nch ? (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (!((ob >> i) & 1u)) mx = max(mx, habs_bits(h[u][i]));
+    }
+  } else {
+    for (int c = rl; c < nch; c += LPR) {
+      uint16_t g[8];
+      load8_half(row, c * 8, K, vec != 0, g);
+      const uint32_t ob = (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (!((ob >> i) & 1u)) mx = max(mx, habs_bits(g[i]));
+    }
+  }
+  mx = wave_max(mx);
+  if (WPR > 1) {
+    if (lane == 0) s_red[wave] = mx;
+    __syncthreads();
+    mx = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+  }
+  const float a = h2f((uint16_t)mx);
+  if (active) {
+    if (CPL > 0) {
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int c = rl + u * LPR;
+        if (c < nch)
+          emit_chunk(h[u], m, c, s_bits[c >> 2], (c & 3) * 8, s_pre[c >> 2], a, ldk, Xq, XO);
+      }
+    } else {
+      for (int c = rl; c < nch; c += LPR) {
+        uint16_t g[8];
+        load8_half(row, c * 8, K, vec != 0, g);
+        emit_chunk(g, m, c, s_bits[c >> 2], (c & 3) * 8, s_pre[c >> 2], a, ldk, Xq, XO);
+      }
+    }
+    if (XO != nullptr)
+      for (int j = total + rl; j < opad; j += LPR)
+        XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = 0;
+    if (rl == 0) x_scale[m] = a;
   }
 }
 
@@ -241,7 +368,7 @@ __global__ void k_zero_half(uint16_t* __restrict__ Y, int64_t count) {
 hipError_t launch_colmax_partial(const uint16_t* X, int M, int K, int ldk, uint16_t* part,
                                  hipStream_t s) {
   const int vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-  dim3 grid(((ldk + 255) / 256) * ((M + kColmaxRowsPerChunk - 1) / kColmaxRowsPerChunk));
+  dim3 grid(((ldk + kColBlock - 1) / kColBlock) * ((M + kRowChunk - 1) / kRowChunk));
   hipLaunchKernelGGL(k_colmax_partial, grid, dim3(256), 0, s, X, M, K, ldk, vec, part);
   return hipGetLastError();
 }
@@ -249,10 +376,19 @@ hipError_t launch_colmax_partial(const uint16_t* X, int M, int K, int ldk, uint1
 hipError_t launch_colmask(const uint16_t* X, const uint16_t* part, int rc, int M, int K,
                           int ldk, float threshold, uint8_t* mask8, uint32_t* mask_bits,
                           hipStream_t s) {
-  dim3 grid((ldk + 255) / 256);
+  dim3 grid((ldk + 63) / 64);
   hipLaunchKernelGGL(k_colmask, grid, dim3(256), 0, s, X, part, rc, M, K, ldk, threshold, mask8,
                      mask_bits);
   return hipGetLastError();
+}
+
+template <int WPR, int CPL>
+static void launch_qr(dim3 grid, size_t lds, hipStream_t s, const uint16_t* X, int M, int K,
+                      int ldk, int vec, int nwb, const uint32_t* mb, int8_t* Xq, float* xs,
+                      uint16_t* XO, int32_t* n_out, int32_t* out_idx, const int8_t* Wq,
+                      const float* ws, int N, uint16_t* WO) {
+  hipLaunchKernelGGL((k_quant_rows<WPR, CPL>), grid, dim3(256), lds, s, X, M, K, ldk, vec, nwb, mb,
+                     Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO);
 }
 
 hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uint32_t* mask_bits,
@@ -260,16 +396,28 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
                              int32_t* out_idx, const int8_t* Wq, const float* w_scale, int N,
                              uint16_t* WO, hipStream_t s) {
   const int vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-  int rpb = (M + 511) / 512;
-  rpb = ((rpb + 3) / 4) * 4;
-  if (rpb < 4) rpb = 4;
-  if (rpb > 32) rpb = 32;
-  const int n_row_blocks = (M + rpb - 1) / rpb;
-  const int n_wo_blocks = WO != nullptr ? (N + 63) / 64 : 0;
-  const size_t lds = (size_t)2 * (ldk / 32) * sizeof(uint32_t);
+  const bool few_rows = M <= 256;  // whole block per row keeps the GPU busy
+  const int wpr = few_rows ? 4 : 1;
+  const int n_row_blocks = few_rows ? M : (M + 3) / 4;
+  const int n_wo_blocks = WO != nullptr ? (N + kWoRows - 1) / kWoRows : 0;
+  const size_t lds = (size_t)2 * (ldk / 32) * sizeof(uint32_t) +
+                     (WO != nullptr ? (size_t)kOListCap * sizeof(int) : 0);
   dim3 grid(n_row_blocks + n_wo_blocks);
-  hipLaunchKernelGGL(k_quant_rows, grid, dim3(256), lds, s, X, M, K, ldk, vec, rpb, n_row_blocks,
-                     mask_bits, Xq, x_scale, XO, n_out, out_idx, Wq, w_scale, N, WO);
+  const int lanes = 64 * wpr;
+  const int cpl_needed = (ldk / 8 + lanes - 1) / lanes;
+#define QR(W, C) launch_qr<W, C>(grid, lds, s, X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out, out_idx, Wq, w_scale, N, WO)
+  if (wpr == 4) {
+    if (cpl_needed <= 4) QR(4, 4);
+    else if (cpl_needed <= 8) QR(4, 8);
+    else QR(4, 0);
+  } else {
+    if (cpl_needed <= 2) QR(1, 2);
+    else if (cpl_needed <= 4) QR(1, 4);
+    else if (cpl_needed <= 8) QR(1, 8);
+    else if (cpl_needed <= 16) QR(1, 16);
+    else QR(1, 0);
+  }
+#undef QR
   return hipGetLastError();
 }
 

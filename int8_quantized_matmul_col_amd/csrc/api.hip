@@ -8,6 +8,7 @@
 
 #include "int8mm.h"
 #include "launch.h"
+#include "tile_layout.h"
 
 namespace {
 
@@ -41,10 +42,11 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
   L.part = off;   off += align_up((size_t)L.rc * L.ldk * 2);
   L.bits = off;   off += align_up((size_t)(L.ldk / 32) * 4);
   L.count = off;  off += kAlign;
+  const size_t Mp = (size_t)i8mm::padded_rows(M), Np = (size_t)i8mm::padded_rows(N);
   L.xscale = off; off += align_up((size_t)M * 4);
-  L.xq = off;     off += align_up((size_t)M * L.ldk);
-  L.xo = off;     off += L.decode ? 0 : align_up((size_t)M * L.ldk * 2);
-  L.wo = off;     off += L.decode ? 0 : align_up((size_t)N * L.ldk * 2);
+  L.xq = off;     off += align_up(Mp * L.ldk);
+  L.xo = off;     off += L.decode ? 0 : align_up(Mp * L.ldk * 2);
+  L.wo = off;     off += L.decode ? 0 : align_up(Np * L.ldk * 2);
   L.total = off < kAlign ? kAlign : off;
   return L;
 }
@@ -145,6 +147,11 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
 extern "C" {
 
 INT8MM_API int64_t int8_weight_ld(int64_t K) { return K < 0 ? -1 : ld_of(K); }
+
+INT8MM_API int64_t int8_weight_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K < 0 || K > INT8MM_MAX_K || N > kMaxRows) return -1;
+  return i8mm::padded_rows(N) * ld_of(K);
+}
 
 INT8MM_API int int8_prepare_weight(const int8mm_half* W, int64_t N, int64_t K, int8_t* Wq, float* w_scale,
                         hipStream_t stream) {

@@ -35,11 +35,13 @@ __device__ __forceinline__ uint32_t habs_bits(uint32_t bits) { return bits & 0x7
 // division is the IEEE-correctly-rounded fp32 division (the library is built
 // without fast-math) and rintf rounds half to even.  For binary16 x and a this
 // equals round-half-even of the exact rational 127*x/a.
+// Branch-free (selects, no divergent control flow around the division).
 __device__ __forceinline__ int quant_code(float x, float a) {
-  if (a == 0.0f) return 0;
-  float q = rintf((127.0f * x) / a);
+  const bool zero = (a == 0.0f);
+  const float d = zero ? 1.0f : a;
+  float q = rintf((127.0f * x) / d);
   q = fminf(fmaxf(q, -127.0f), 127.0f);
-  return (int)q;
+  return zero ? 0 : (int)q;
 }
 
 // Dequantized outlier weight value fp16(fp32(fp32(q) * a_w) / 127).

@@ -16,6 +16,7 @@
 // and the epilogue writes Y = fp16(fp32(C)*a_x*a_w/127^2 + Y_O).
 #include "device_common.h"
 #include "launch.h"
+#include "tile_layout.h"
 
 namespace i8mm {
 
@@ -57,11 +58,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   const int ml = lane & 15;   // row of the Xq fragment / column of the result
   const int kq = (lane >> 4) * 16;  // byte offset of this lane inside the 64-byte step
 
-  const int8_t* xrow = Xq + (size_t)min(ml, M - 1) * ldk + kq;
+  // panel-tiled operands (tile_layout.h): step s of row r is at
+  // tiled_offset(r, 64*s + kq) = tiled_offset(r, kq) + s * 16 KiB; the 16 rows
+  // of a group are 1 KiB contiguous per step
+  const int8_t* xrow = Xq + tiled_offset(ml, kq, ldk);
   const bool xvalid = ml < M;
   const int8_t* wrow[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) wrow[g] = Wq + (size_t)min(n_base + g * 16 + ml, N - 1) * ldk + kq;
+  for (int g = 0; g < G; ++g) wrow[g] = Wq + tiled_offset(n_base + g * 16 + ml, kq, ldk);
 
   v4i acc[G];
   v4f acco[G];
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   }
 
   for (int s = s0; s < s1; ++s) {
-    const size_t off = (size_t)s * 64;
+    const size_t off = (size_t)s * kTileBytes;
     v4i b[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) b[g] = *reinterpret_cast<const v4i*>(wrow[g] + off);

@@ -7,115 +7,164 @@
 // "PyTorch 2.9 supports LLM.int8()", section 3: results merged at the end.)
 //
 // One workgroup = 256x256 output tile, 4 waves in a 2x2 arrangement, each
-// wave a 128x128 block held as 4x4 v_mfma_i32_32x32x32_i8 accumulators.  The
-// K loop stages 64-byte slices of Xq and Wq through double-buffered LDS
-// (one barrier per step); 16-byte chunks are XOR-swizzled so that both the
-// 16-byte stores and the ds_read_b128 fragment reads are bank-conflict free.
-// After the int8 loop the accumulators are rescaled to fp32 in place and the
-// outlier slice (|O| rounded up to 32 columns of fp16) runs through the same
-// pipeline on v_mfma_f32_32x32x16_f16, accumulating on top -- a 64-byte fp16
-// slice has exactly the byte layout of a 64-byte int8 slice, so the staging
-// and fragment code is shared.  |O| is read on the device: no host sync.
+// wave a 128x128 block held as 4x4 v_mfma_i32_32x32x32_i8 accumulators
+// (256 AGPRs).  Operands are panel-tiled in memory (tile_layout.h), so one
+// 64-byte K step of a 256-row panel is 16 KiB contiguous: every wave load
+// instruction moves 1 KiB of whole cache lines straight into LDS
+// (global_load_lds_dwordx4: no VGPR staging, no ds_write).  Four LDS stages
+// let loads run two steps ahead and let the first fragments of step k+1 be
+// read before the barrier that ends step k; one barrier per step.
 //
-// MFMA operand convention: for both instructions lane l supplies row (l%32)
-// of its operand and 16 bytes of K; A and B fragments are loaded with the
-// same K mapping, so the pairing of K indices is consistent whatever order
-// the hardware assigns inside the 16 bytes (the sum over K is order-free
-// for the exact int8 product and within fp32 rounding for fp16).
+// The outlier slice (|O| rounded up to 32 fp16 columns: 64 bytes per row per
+// step, the same byte shape as an int8 step) is appended to the same
+// pipeline as extra steps on v_mfma_f32_32x32x16_f16: their loads are issued
+// during the last int8 steps, the int32 accumulators are rescaled to fp32 in
+// place in between, and the fp16 products accumulate on top.  |O| is read on
+// the device: no host synchronisation.
+//
+// MFMA operand convention: lane l supplies row (l%32) of its operand and 16
+// bytes of K; A and B fragments use the same K mapping, so the pairing of K
+// indices is consistent whatever order the hardware assigns inside the 16
+// bytes (exact for the int8 sum, within fp32 rounding for fp16).
 #include "device_common.h"
 #include "launch.h"
+#include "tile_layout.h"
 
 namespace i8mm {
 
 namespace {
 
-constexpr int BM = 256;
-constexpr int BN = 256;
-constexpr int BKB = 64;  // bytes of K per pipeline step
+constexpr int BM = kPanelRows;  // 256
+constexpr int BN = kPanelRows;
 constexpr int NT = 256;
+constexpr int NBUF = 4;  // LDS stages of 256 rows x 64 bytes per operand
 
 struct Smem {
-  v4i a[2][BM * 4];
-  v4i b[2][BN * 4];
+  v4i a[NBUF][BM * 4];
+  v4i b[NBUF][BN * 4];
   float sx[BM];
   float sw[BN];
 };
 
-__device__ __forceinline__ int swz(int row, int ch) { return row * 4 + (ch ^ ((row >> 1) & 3)); }
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-struct Stage {
+// LDS slot of 16-byte chunk `ch` (0..3) of tile row `row`.  gfx950 LDS serves
+// a 16-byte read in groups of 16 lanes (64 banks, 256 B/clk): 16 consecutive
+// rows then hit 16 distinct slots when the chunk is XORed with bits 2..3 of
+// the row.  The direct-to-LDS loads fill 64 consecutive slots per wave
+// instruction, so the swizzle is applied on the global-address side.
+__device__ __forceinline__ int swz(int row, int ch) { return row * 4 + (ch ^ ((row >> 2) & 3)); }
+
+// Source of pipeline step s: int8 steps first, then fp16 outlier steps.
+struct Src {
+  const char* A;  // panel-tiled; the tile's panel already applied
+  const char* B;
+  const char* AO;
+  const char* BO;
+  int nk8;  // number of int8 steps
+};
+
+// Issue the loads of step s into stage `buf`: 4 instructions per operand per
+// wave, each 64 lanes x 16 bytes = a 1 KiB slice of the 16 KiB block.
+__device__ __forceinline__ void gload(Smem& sm, int buf, const Src& src, int s, int wave,
+                                      int lane) {
+  const char* a;
+  const char* b;
+  if (s < src.nk8) {
+    a = src.A + (size_t)s * kTileBytes;
+    b = src.B + (size_t)s * kTileBytes;
+  } else {
+    a = src.AO + (size_t)(s - src.nk8) * kTileBytes;
+    b = src.BO + (size_t)(s - src.nk8) * kTileBytes;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s0 = (i * 4 + wave) * 64;
+    const int slot = s0 + lane;
+    const int row = slot >> 2;
+    const int ch = (slot & 3) ^ ((row >> 2) & 3);
+    const int off = row * 64 + ch * 16;
+    __builtin_amdgcn_global_load_lds((const void*)(a + off), (lds_ptr_t)&sm.a[buf][s0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(b + off), (lds_ptr_t)&sm.b[buf][s0], 16, 0, 0);
+  }
+}
+
+// MFMA operand fragments of one 32-byte K sub-step for the wave's 4x4 tiles.
+struct Frag {
   v4i a[4];
   v4i b[4];
 };
 
-// Global -> registers for one 64-byte K step.  Rows past the matrix end are
-// clamped to the last row (their results are never stored).
-__device__ __forceinline__ void gload(Stage& st, const char* __restrict__ A, size_t lda, int a_last,
-                                      int m0, const char* __restrict__ B, size_t ldb, int b_last,
-                                      int n0, size_t kbyte) {
+__device__ __forceinline__ void fload(Frag& f, const Smem& sm, int buf, int kk, int wm0, int wn0,
+                                      int lane) {
+  const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + NT * i;
-    const int row = c >> 2, ch = c & 3;
-    const int ra = min(m0 + row, a_last);
-    const int rb = min(n0 + row, b_last);
-    st.a[i] = *reinterpret_cast<const v4i*>(A + (size_t)ra * lda + kbyte + ch * 16);
-    st.b[i] = *reinterpret_cast<const v4i*>(B + (size_t)rb * ldb + kbyte + ch * 16);
-  }
+  for (int i = 0; i < 4; ++i) f.a[i] = sm.a[buf][swz(wm0 + i * 32 + (lane & 31), ch)];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b[j] = sm.b[buf][swz(wn0 + j * 32 + (lane & 31), ch)];
 }
 
-__device__ __forceinline__ void sstore(Smem& sm, int buf, const Stage& st) {
+template <bool F16>
+__device__ __forceinline__ void mma(const Frag& f, v16i (&acc)[4][4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + NT * i;
-    const int row = c >> 2, ch = c & 3;
-    sm.a[buf][swz(row, ch)] = st.a[i];
-    sm.b[buf][swz(row, ch)] = st.b[i];
-  }
-}
-
-__device__ __forceinline__ void mma_i8(const Smem& sm, int buf, int wm0, int wn0, int lane,
-                                       v16i (&acc)[4][4]) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int ch = kk * 2 + (lane >> 5);
-    v4i a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = sm.a[buf][swz(wm0 + i * 32 + (lane & 31), ch)];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = sm.b[buf][swz(wn0 + j * 32 + (lane & 31), ch)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-// acc holds fp32 bit patterns here (reinterpreted in place, no second set
-// of 256 accumulator registers).
-__device__ __forceinline__ void mma_f16(const Smem& sm, int buf, int wm0, int wn0, int lane,
-                                        v16i (&acc)[4][4]) {
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int ch = kk * 2 + (lane >> 5);
-    v8h a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = __builtin_bit_cast(v8h, sm.a[buf][swz(wm0 + i * 32 + (lane & 31), ch)]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = __builtin_bit_cast(v8h, sm.b[buf][swz(wn0 + j * 32 + (lane & 31), ch)]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (F16) {
+        // acc holds fp32 bit patterns here (reinterpreted in place)
         acc[i][j] = __builtin_bit_cast(
-            v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j],
-                                                         __builtin_bit_cast(v16f, acc[i][j]), 0, 0, 0));
+            v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, f.a[i]),
+                                                         __builtin_bit_cast(v8h, f.b[j]),
+                                                         __builtin_bit_cast(v16f, acc[i][j]), 0,
+                                                         0, 0));
+      } else {
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+}
+
+// s_waitcnt: vmcnt <= 8 (the loads issued in the current step may stay in
+// flight) and lgkmcnt 0; or everything.
+__device__ __forceinline__ void wait_prev_step() {
+  __builtin_amdgcn_s_waitcnt((8 & 0xf) | (7 << 4) | (0 << 8) | ((8 >> 4) << 14));
+}
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// One pipeline step: fragments of sub-step 1 while sub-step 0 computes, the
+// next step's sub-step-0 fragments while sub-step 1 computes, the loads of
+// step kt+3; then wait for the loads of step kt+2 and this wave's LDS reads,
+// and the barrier.  Branch-free: loads past the end are clamped to the last
+// step (in bounds, landing in a stage that is not read again).
+template <bool F16>
+__device__ __forceinline__ void step(Smem& sm, v16i (&acc)[4][4], Frag& f0, Frag& f1,
+                                     const Src& src, int kt, int last, int wm0, int wn0, int wave,
+                                     int lane) {
+  const int cur = kt & 3, nxt = (kt + 1) & 3, far = (kt + 3) & 3;
+  fload(f1, sm, cur, 1, wm0, wn0, lane);
+  mma<F16>(f0, acc);
+  fload(f0, sm, nxt, 0, wm0, wn0, lane);
+  mma<F16>(f1, acc);
+  gload(sm, far, src, min(kt + 3, last), wave, lane);
+  // sub-step-1 reads over the first 8 MFMAs, prefetch reads over the third
+  // group of 8, the 8 global loads over the last 8 MFMAs
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+  }
+  wait_prev_step();
+  __builtin_amdgcn_s_barrier();
 }
 
 // Row (within the wave block) of accumulator element r of lane `lane` for a
@@ -158,24 +207,31 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
 
+  const int nk8 = ldk / kTileK;
+  const int nk16 = MODE == 0 ? (*n_out + 31) / 32 : 0;
+  const int last = nk8 + nk16 - 1;
+  Src src;
+  src.A = (const char*)Xq + (size_t)tm * nk8 * kTileBytes;
+  src.B = (const char*)Wq + (size_t)tn * nk8 * kTileBytes;
+  src.AO = (const char*)XO + (size_t)tm * (2 * nk8) * kTileBytes;  // fp16 rows: 2*ldk bytes
+  src.BO = (const char*)WO + (size_t)tn * (2 * nk8) * kTileBytes;
+  src.nk8 = nk8;
+
+  // prologue: stages 0..2
+  gload(sm, 0, src, 0, wave, lane);
+  gload(sm, 1, src, min(1, last), wave, lane);
+  gload(sm, 2, src, min(2, last), wave, lane);
+  wait_all();
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  fload(f0, sm, 0, 0, wm0, wn0, lane);
+
   // ---- int8 x int8 -> int32 over all K (outlier columns of Xq are zero)
-  const int nk = ldk / BKB;
-  {
-    Stage st;
-    gload(st, (const char*)Xq, ldk, M - 1, m0, (const char*)Wq, ldk, N - 1, n0, 0);
-    sstore(sm, 0, st);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk)
-        gload(st, (const char*)Xq, ldk, M - 1, m0, (const char*)Wq, ldk, N - 1, n0,
-              (size_t)(kt + 1) * BKB);
-      mma_i8(sm, kt & 1, wm0, wn0, lane, acc);
-      if (kt + 1 < nk) sstore(sm, (kt + 1) & 1, st);
-      __syncthreads();
-    }
-  }
+  int kt = 0;
+  for (; kt < nk8; ++kt) step<false>(sm, acc, f0, f1, src, kt, last, wm0, wn0, wave, lane);
 
   if (MODE == 1) {
+    wait_all();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -193,50 +249,78 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   {
     const int t = threadIdx.x;
     sm.sx[t] = x_scale[min(m0 + t, M - 1)];
-    sm.sw[t] = w_scale[min(n0 + t, N - 1)];
+    sm.sw[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    // the 16 row scales of this lane for row block i: 4 runs of 4 rows
+    float sx[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4f v = *reinterpret_cast<const v4f*>(&sm.sx[wm0 + i * 32 + q * 8 + (lane >> 5) * 4]);
+      sx[q * 4 + 0] = v[0];
+      sx[q * 4 + 1] = v[1];
+      sx[q * 4 + 2] = v[2];
+      sx[q * 4 + 3] = v[3];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float sw = sm.sw[wn0 + j * 32 + (lane & 31)] * kInv127Sq;
+      const float sw = sm.sw[wn0 + j * 32 + (lane & 31)];
       v16f f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        f[r] = (float)acc[i][j][r] * (sm.sx[wm0 + i * 32 + acc_row(r, lane)] * sw);
+      for (int r = 0; r < 16; ++r) f[r] = (float)acc[i][j][r] * (sx[r] * sw);
       acc[i][j] = __builtin_bit_cast(v16i, f);
-    }
-
-  // ---- fp16 outlier slice: X_O [M][ldk] . W_O [N][ldk]^T over ceil(|O|/32) steps
-  const int n_steps = (*n_out + 31) / 32;
-  if (n_steps > 0) {
-    const size_t ldo = (size_t)ldk * 2;  // bytes per row of X_O / W_O
-    Stage st;
-    gload(st, (const char*)XO, ldo, M - 1, m0, (const char*)WO, ldo, N - 1, n0, 0);
-    sstore(sm, 0, st);
-    __syncthreads();
-    for (int ks = 0; ks < n_steps; ++ks) {
-      if (ks + 1 < n_steps)
-        gload(st, (const char*)XO, ldo, M - 1, m0, (const char*)WO, ldo, N - 1, n0,
-              (size_t)(ks + 1) * BKB);
-      mma_f16(sm, ks & 1, wm0, wn0, lane, acc);
-      if (ks + 1 < n_steps) sstore(sm, (ks + 1) & 1, st);
-      __syncthreads();
     }
   }
 
-  // ---- store fp16 Y
+  // ---- fp16 outlier steps (their first loads are already in flight)
+  for (; kt <= last; ++kt) step<true>(sm, acc, f0, f1, src, kt, last, wm0, wn0, wave, lane);
+
+  // ---- store fp16 Y through LDS: each wave converts its 128x128 block to
+  // fp16 in two 64-row halves, writes them to a private 16 KiB LDS region,
+  // then stores whole 256-byte row segments with 16-byte stores.
+  wait_all();
+  __syncthreads();
+  uint16_t* ys = reinterpret_cast<uint16_t*>(&sm.a[0][0]) + wave * (64 * 128);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = half * 2 + ii;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm0 + i * 32 + acc_row(r, lane);
-        const int n = n0 + wn0 + j * 32 + (lane & 31);
-        if (m < M && n < N) Y[(size_t)m * N + n] = f2h(__builtin_bit_cast(v16f, acc[i][j])[r]);
+      for (int j = 0; j < 4; ++j) {
+        const v16f f = __builtin_bit_cast(v16f, acc[i][j]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ys[(ii * 32 + acc_row(r, lane)) * 128 + j * 32 + (lane & 31)] = f2h(f[r]);
       }
+    }
+    // wave-private region: only this wave's LDS traffic must be ordered
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int n_col = n0 + wn0 + (lane & 15) * 8;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int rl = p * 4 + (lane >> 4);  // row within the 64-row half
+      const int m = m0 + wm0 + half * 64 + rl;
+      const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 128 + (lane & 15) * 8);
+      if (m < M) {
+        if (n_col + 8 <= N && (N & 7) == 0) {
+          *reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col) = v;
+        } else {
+          const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int ldk,

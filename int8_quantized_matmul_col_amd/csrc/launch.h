@@ -9,7 +9,7 @@
 namespace i8mm {
 
 // Rows of X reduced by one block of the column-absmax pass (prefill path).
-constexpr int kColmaxRowsPerChunk = 256;
+constexpr int kColmaxRowsPerChunk = 64;
 
 hipError_t launch_prepare_weight(const uint16_t* W, int N, int K, int ldk, int8_t* Wq,
                                  float* w_scale, hipStream_t s);

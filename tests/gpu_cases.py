@@ -23,12 +23,13 @@ def check_prepare(mm, W16: np.ndarray):
     N, K = W16.shape
     Wq_d, s_d = mm.int8_prepare_weight(to_dev(W16))
     torch.cuda.synchronize()
-    Wq = Wq_d.cpu().numpy()
+    Wq = mm.untile(Wq_d, Wq_d.shape[0]).cpu().numpy()  # [Np][ldk] row-major
     s = s_d.cpu().numpy()
     Wq_r, s_r = ref.prepare_weight_ref(W16)
     assert np.array_equal(s, s_r), "w_scale"
-    assert np.array_equal(Wq[:, :K], Wq_r), "Wq"
-    assert not Wq[:, K:].any(), "Wq padding"
+    assert np.array_equal(Wq[:N, :K], Wq_r), "Wq"
+    assert not Wq[:N, K:].any(), "Wq padding columns"
+    assert not Wq[N:].any(), "Wq padding rows"
     return Wq_d, s_d, Wq_r, s_r
 
 
@@ -58,7 +59,6 @@ def check_y(Y: np.ndarray, Y_ref: np.ndarray, X16, Wq_r, s_r, n_out, what="Y"):
 def run_stages(mm, X16, Wq_d, s_d, t, Wq_r, s_r):
     """Stage-by-stage comparison; returns the oracle result dict."""
     M, K = X16.shape
-    N = Wq_r.shape[0]
     X_d = to_dev(X16)
     o = mm.int8_matmul_stages(X_d, Wq_d, s_d, threshold=t, want_c=True)
     torch.cuda.synchronize()

@@ -39,7 +39,7 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     fns = header_functions()
-    assert fns == sorted(["int8_weight_ld", "int8_prepare_weight", "int8_matmul_workspace_size",
+    assert fns == sorted(["int8_weight_ld", "int8_weight_bytes", "int8_prepare_weight", "int8_matmul_workspace_size",
                           "int8_matmul", "int8_matmul_stages", "int8_matmul_profiled", "int8mm_strerror",
                           "int8mm_last_hip_error"])
     assert set(fns) == set(binding.SIGNATURES)
@@ -73,6 +73,26 @@ def test_weight_ld(lib):
     for K, ld in [(0, 0), (1, 64), (63, 64), (64, 64), (65, 128), (4096, 4096), (11008, 11008),
                   (133144, 133184)]:
         assert lib.int8_weight_ld(K) == ld
+
+
+def test_weight_bytes(lib):
+    assert lib.int8_weight_bytes(-1, 8) == -1 and lib.int8_weight_bytes(8, -1) == -1
+    assert lib.int8_weight_bytes(8, binding.INT8MM_MAX_K + 1) == -1
+    assert lib.int8_weight_bytes(0, 64) == 0
+    assert lib.int8_weight_bytes(1, 1) == 256 * 64          # one padded panel
+    assert lib.int8_weight_bytes(4096, 4096) == 4096 * 4096
+    assert lib.int8_weight_bytes(300, 520) == 512 * 576
+
+
+def test_untile_matches_documented_layout():
+    import torch
+    Rp, L = 512, 128
+    flat = torch.arange(Rp * L, dtype=torch.int32) % 251
+    buf = flat.to(torch.uint8).view(Rp, L)
+    rm = binding.untile(buf, 300)
+    for (r, b) in [(0, 0), (5, 70), (255, 127), (256, 0), (299, 64), (257, 127)]:
+        off = ((r // 256) * (L // 64) + b // 64) * 16384 + (r % 256) * 64 + b % 64
+        assert int(rm[r, b]) == int(flat[off]) % 256
 
 
 def test_workspace_size(lib):

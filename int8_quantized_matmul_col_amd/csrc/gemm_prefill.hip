@@ -175,6 +175,154 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
 
 }  // namespace
 
+// Many outlier columns (more than three fp16 steps): dequantize the int32
+// accumulators in place and continue the pipeline over the fp16 steps on
+// top.  Kept out of line so that its register pressure does not shape the
+// common path's allocation; it recomputes the whole tile.
+__device__ __attribute__((noinline)) void gemm_tile_many_outliers(
+    Smem& sm, const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int ldk,
+    const float* __restrict__ x_scale, const float* __restrict__ w_scale,
+    const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
+    const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+
+  // XCD-aware tile order: consecutive workgroups go round-robin to the 8
+  // XCDs, so give each XCD a contiguous run of tiles, and walk the tiles in
+  // groups of 4 tile-rows so the run shares A and B panels in its L2.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int G = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  constexpr int GROUP = 4;
+  const int per_group = GROUP * tiles_n;
+  const int first_m = (L / per_group) * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (L % per_group) % gsz;
+  const int tn = (L % per_group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  v16i acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+
+  const int nk8 = ldk / kTileK;
+  const int nk16 = (*n_out + 31) / 32;
+  const int last = nk8 + nk16 - 1;
+  Src src;
+  src.A = (const char*)Xq + (size_t)tm * nk8 * kTileBytes;
+  src.B = (const char*)Wq + (size_t)tn * nk8 * kTileBytes;
+  src.AO = (const char*)XO + (size_t)tm * (2 * nk8) * kTileBytes;  // fp16 rows: 2*ldk bytes
+  src.BO = (const char*)WO + (size_t)tn * (2 * nk8) * kTileBytes;
+  src.nk8 = nk8;
+
+  // prologue: stages 0..2
+  gload(sm, 0, src, 0, wave, lane);
+  gload(sm, 1, src, min(1, last), wave, lane);
+  gload(sm, 2, src, min(2, last), wave, lane);
+  wait_all();
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  fload(f0, sm, 0, 0, wm0, wn0, lane);
+
+  // ---- int8 x int8 -> int32 over all K (outlier columns of Xq are zero)
+  int kt = 0;
+  for (; kt < nk8; ++kt) step<false>(sm, acc, f0, f1, src, kt, last, wm0, wn0, wave, lane);
+
+  if (false) {
+    wait_all();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm0 + i * 32 + acc_row(r, lane);
+          const int n = n0 + wn0 + j * 32 + (lane & 31);
+          if (m < M && n < N) C[(size_t)m * N + n] = acc[i][j][r];
+        }
+    return;
+  }
+
+  // ---- scales of the tile's rows and columns
+  {
+    const int t = threadIdx.x;
+    sm.sx[t] = x_scale[min(m0 + t, M - 1)];
+    sm.sw[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
+  }
+  const int n_col = n0 + wn0 + (lane & 15) * 8;
+  const bool vec_store = (N & 7) == 0;
+
+  // ---- many outlier columns: dequantize in place, fp32(C) * a_x[m] * a_w[n]
+  // / 127^2, and continue the pipeline over the fp16 steps on top.
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float sx[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4f v = *reinterpret_cast<const v4f*>(&sm.sx[wm0 + i * 32 + q * 8 + (lane >> 5) * 4]);
+      sx[q * 4 + 0] = v[0];
+      sx[q * 4 + 1] = v[1];
+      sx[q * 4 + 2] = v[2];
+      sx[q * 4 + 3] = v[3];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sw = sm.sw[wn0 + j * 32 + (lane & 31)];
+      v16f f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f[r] = (float)acc[i][j][r] * (sx[r] * sw);
+      acc[i][j] = __builtin_bit_cast(v16i, f);
+    }
+  }
+  for (; kt <= last; ++kt) step<true>(sm, acc, f0, f1, src, kt, last, wm0, wn0, wave, lane);
+
+  // store fp16 Y through LDS: two 64-row halves per wave, 16 KiB each
+  wait_all();
+  __syncthreads();
+  uint16_t* ys = reinterpret_cast<uint16_t*>(&sm.a[0][0]) + wave * (64 * 128);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = half * 2 + ii;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v16f f = __builtin_bit_cast(v16f, acc[i][j]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ys[(ii * 32 + acc_row(r, lane)) * 128 + j * 32 + (lane & 31)] = f2h(f[r]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int rl = p * 4 + (lane >> 4);  // row within the 64-row half
+      const int m = m0 + wm0 + half * 64 + rl;
+      const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 128 + (lane & 15) * 8);
+      if (m < M) {
+        if (vec_store && n_col + 8 <= N) {
+          *reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col) = v;
+        } else {
+          const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+
 template <int MODE>  // 0: Y (fused epilogue), 1: int32 C
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
 k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int ldk,
@@ -183,6 +331,10 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
                const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y,
                int32_t* __restrict__ C) {
   __shared__ Smem sm;
+  if (MODE == 0 && (*n_out + 31) / 32 > 3) {
+    gemm_tile_many_outliers(sm, Xq, Wq, M, N, ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
 
@@ -245,82 +397,92 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     return;
   }
 
-  // ---- dequantize in place: fp32(C) * a_x[m] * a_w[n] / 127^2
+  // ---- scales of the tile's rows and columns
   {
     const int t = threadIdx.x;
     sm.sx[t] = x_scale[min(m0 + t, M - 1)];
     sm.sw[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
   }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // the 16 row scales of this lane for row block i: 4 runs of 4 rows
-    float sx[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const v4f v = *reinterpret_cast<const v4f*>(&sm.sx[wm0 + i * 32 + q * 8 + (lane >> 5) * 4]);
-      sx[q * 4 + 0] = v[0];
-      sx[q * 4 + 1] = v[1];
-      sx[q * 4 + 2] = v[2];
-      sx[q * 4 + 3] = v[3];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float sw = sm.sw[wn0 + j * 32 + (lane & 31)];
-      v16f f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) f[r] = (float)acc[i][j][r] * (sx[r] * sw);
-      acc[i][j] = __builtin_bit_cast(v16i, f);
-    }
-  }
+  const int n_col = n0 + wn0 + (lane & 15) * 8;
+  const bool vec_store = (N & 7) == 0;
 
-  // ---- fp16 outlier steps (their first loads are already in flight)
-  for (; kt <= last; ++kt) step<true>(sm, acc, f0, f1, src, kt, last, wm0, wn0, wave, lane);
-
-  // ---- store fp16 Y through LDS: each wave converts its 128x128 block to
-  // fp16 in two 64-row halves, writes them to a private 16 KiB LDS region,
-  // then stores whole 256-byte row segments with 16-byte stores.
-  wait_all();
-  __syncthreads();
-  uint16_t* ys = reinterpret_cast<uint16_t*>(&sm.a[0][0]) + wave * (64 * 128);
+  {
+    // Few outlier steps: their operands were prefetched into LDS stages
+    // (nk8 + s) & 3 by the int8 loop.  Per 32-row group i: the outlier
+    // product into a 64-register temporary, then Y = fp32(C)*s + Y_O read
+    // straight from the int32 accumulators, converted to fp16, staged in the
+    // free LDS stage (nk8 + 3) & 3 (8 KiB per wave) and stored as 256-byte
+    // row segments.
+    wait_all();
+    __syncthreads();
+    const int fs = (nk8 + 3) & 3;
+    uint16_t* ys = reinterpret_cast<uint16_t*>(wave < 2 ? &sm.a[fs][0] : &sm.b[fs][0]) +
+                   (wave & 1) * (32 * 128);
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+    for (int i = 0; i < 4; ++i) {
+      // row group i: scaled int8 part first (its accumulator registers are
+      // then free for the fp16 MFMAs), outlier products accumulated on top
+      float sx[16];
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = half * 2 + ii;
+      for (int q = 0; q < 4; ++q) {
+        const v4f v =
+            *reinterpret_cast<const v4f*>(&sm.sx[wm0 + i * 32 + q * 8 + (lane >> 5) * 4]);
+        sx[q * 4 + 0] = v[0];
+        sx[q * 4 + 1] = v[1];
+        sx[q * 4 + 2] = v[2];
+        sx[q * 4 + 3] = v[3];
+      }
+      v16f y[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const v16f f = __builtin_bit_cast(v16f, acc[i][j]);
+        const float sw = sm.sw[wn0 + j * 32 + (lane & 31)];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ys[(ii * 32 + acc_row(r, lane)) * 128 + j * 32 + (lane & 31)] = f2h(f[r]);
+        for (int r = 0; r < 16; ++r) y[j][r] = (float)acc[i][j][r] * (sx[r] * sw);
       }
-    }
-    // wave-private region: only this wave's LDS traffic must be ordered
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int n_col = n0 + wn0 + (lane & 15) * 8;
+      for (int st = 0; st < nk16; ++st) {
+        const int stg = (nk8 + st) & 3;
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int rl = p * 4 + (lane >> 4);  // row within the 64-row half
-      const int m = m0 + wm0 + half * 64 + rl;
-      const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 128 + (lane & 15) * 8);
-      if (m < M) {
-        if (n_col + 8 <= N && (N & 7) == 0) {
-          *reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col) = v;
-        } else {
-          const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+        for (int kk = 0; kk < 2; ++kk) {
+          const int ch = kk * 2 + (lane >> 5);
+          const v8h a = __builtin_bit_cast(v8h, sm.a[stg][swz(wm0 + i * 32 + (lane & 31), ch)]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
+          for (int j = 0; j < 4; ++j) {
+            const v8h b = __builtin_bit_cast(v8h, sm.b[stg][swz(wn0 + j * 32 + (lane & 31), ch)]);
+            y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, y[j], 0, 0, 0);
+          }
         }
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ys[acc_row(r, lane) * 128 + j * 32 + (lane & 31)] = f2h(y[j][r]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int rl = p * 4 + (lane >> 4);  // row within the 32-row group
+        const int m = m0 + wm0 + i * 32 + rl;
+        const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 128 + (lane & 15) * 8);
+        if (m < M) {
+          if (vec_store && n_col + 8 <= N) {
+            *reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col) = v;
+          } else {
+            const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return;
   }
+
 }
 
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int ldk,

@@ -164,9 +164,9 @@ INT8MM_API int int8_matmul_stages(const int8mm_half* X, int64_t M, int64_t K,
 
 /*
  * int8_matmul_profiled -- int8_matmul, plus two caller-created HIP events
- * recorded on `stream` immediately before and after the launch of the
- * matmul kernel (the tile GEMM, or the decode kernel for M <= 16), so that
- * its own duration can be read with hipEventElapsedTime.  Either event may
+ * that the dispatch of the matmul kernel (the tile GEMM, or the decode
+ * kernel for M <= 16) stamps with its own start and end times, so that the
+ * kernel's duration can be read with hipEventElapsedTime.  Either event may
  * be NULL.  Same computation, arguments and errors as int8_matmul.
  */
 INT8MM_API int int8_matmul_profiled(const int8mm_half* X, int64_t M, int64_t K,

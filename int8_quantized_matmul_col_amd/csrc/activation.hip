@@ -29,9 +29,9 @@ constexpr int kRowChunk = kColmaxRowsPerChunk;
 
 // ---------------------------------------------------------------- column absmax
 
-// grid = ceil(ldk/512) column blocks x ceil(M/64) row chunks (column block
+// grid = ceil(ldk/512) column blocks x ceil(M/kRowChunk) row chunks (column block
 // fastest).  Block 256 = 64 column lanes x 4 row lanes; each lane reads 8
-// consecutive columns (16 bytes) of 16 rows of the chunk, all loads issued
+// consecutive columns (16 bytes) of kRowChunk/4 rows of the chunk, all loads issued
 // before use.  A wave reads one 1 KiB row segment per load instruction.
 __global__ __launch_bounds__(256) void k_colmax_partial(const uint16_t* __restrict__ X, int M,
                                                         int K, int ldk, int vec,
@@ -43,9 +43,10 @@ __global__ __launch_bounds__(256) void k_colmax_partial(const uint16_t* __restri
   const int r0 = rcix * kRowChunk;
   uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (c0 < K) {
-    uint16_t h[16][8];
+    constexpr int kU = kRowChunk / 4;  // rows per lane
+    uint16_t h[kU][8];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int r = r0 + ty + 4 * u;
       if (r < M) {
         load8_half(X + (size_t)r * K, c0, K, vec != 0, h[u]);
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(256) void k_colmax_partial(const uint16_t* __restri
       }
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int i = 0; i < 8; ++i) mx[i] = max(mx[i], habs_bits(h[u][i]));
   }
@@ -83,26 +84,31 @@ __global__ __launch_bounds__(256) void k_colmask(const uint16_t* __restrict__ X,
   const int col = blockIdx.x * 64 + cl;
   uint32_t v = 0;
   if (col < K) {
-    const int n = part != nullptr ? rc : M;
-    int r = pl;
-    for (; r + 12 < n; r += 16) {
-      uint32_t a0, a1, a2, a3;
-      if (part != nullptr) {
-        a0 = part[(size_t)r * ldk + col];
-        a1 = part[(size_t)(r + 4) * ldk + col];
-        a2 = part[(size_t)(r + 8) * ldk + col];
-        a3 = part[(size_t)(r + 12) * ldk + col];
-      } else {
-        a0 = habs_bits(X[(size_t)r * K + col]);
-        a1 = habs_bits(X[(size_t)(r + 4) * K + col]);
-        a2 = habs_bits(X[(size_t)(r + 8) * K + col]);
-        a3 = habs_bits(X[(size_t)(r + 12) * K + col]);
+    // 16 independent loads per lane and round (one round for rc <= 64)
+    constexpr int kU = 16;
+    if (part != nullptr) {
+      for (int r0 = pl; r0 < rc; r0 += 4 * kU) {
+        uint32_t a[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int r = r0 + 4 * u;
+          a[u] = r < rc ? (uint32_t)part[(size_t)r * ldk + col] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v = max(v, a[u]);
       }
-      v = max(v, max(max(a0, a1), max(a2, a3)));
+    } else {
+      for (int r0 = pl; r0 < M; r0 += 4 * kU) {
+        uint32_t a[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int r = r0 + 4 * u;
+          a[u] = r < M ? habs_bits(X[(size_t)r * K + col]) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v = max(v, a[u]);
+      }
     }
-    for (; r < n; r += 4)
-      v = max(v, part != nullptr ? (uint32_t)part[(size_t)r * ldk + col]
-                                 : habs_bits(X[(size_t)r * K + col]));
   }
   __shared__ uint32_t s[4][64];
   s[pl][cl] = v;
@@ -174,44 +180,320 @@ __device__ __forceinline__ int select_outlier(const uint32_t* s_bits, const int*
 
 namespace {
 
-// Quantize, store and compact one 8-column chunk c of row m (the chunk's mask
-// bits are `word >> sh`).
-__device__ __forceinline__ void emit_chunk(const uint16_t h[8], int m, int c, uint32_t word, int sh,
-                                           int pre, float a, int ldk, int8_t* __restrict__ Xq,
-                                           uint16_t* __restrict__ XO) {
-  const uint32_t ob = (word >> sh) & 0xffu;
+// |v - rint(v)| above this sends a lane to the IEEE division (quant8).
+constexpr float kTieGuard = 0.5f - 0x1p-14f;
+
+// binary16 bits of column i (0..7) of a 16-byte chunk.
+__device__ __forceinline__ uint32_t half_at(const uint4& w, int i) {
+  const uint32_t d = i < 2 ? w.x : i < 4 ? w.y : i < 6 ? w.z : w.w;
+  return (i & 1) ? (d >> 16) : (d & 0xffffu);
+}
+
+// 16-byte chunk of 8 binary16 values at row[c0], zero past K.
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ row, int c0, int K,
+                                            bool vec) {
+  if (vec && c0 + 8 <= K) return *reinterpret_cast<const uint4*>(row + c0);
+  uint32_t d[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t lo = (c0 + 2 * p < K) ? row[c0 + 2 * p] : 0u;
+    const uint32_t hi = (c0 + 2 * p + 1 < K) ? row[c0 + 2 * p + 1] : 0u;
+    d[p] = lo | (hi << 16);
+  }
+  return uint4{d[0], d[1], d[2], d[3]};
+}
+
+// Bytes (or binary16 halves) of a chunk that belong to regular columns: the
+// mask bits ob (bit i = column i is an outlier) expanded to keep-masks.
+__device__ __forceinline__ uint32_t keep_bytes(uint32_t ob4) {
+  uint32_t k = 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if ((ob4 >> i) & 1u) k &= ~(0xffu << (8 * i));
+  return k;
+}
+__device__ __forceinline__ uint32_t keep_halves(uint32_t ob2) {
+  return ((ob2 & 1u) ? 0u : 0xffffu) | ((ob2 & 2u) ? 0u : 0xffff0000u);
+}
+
+// Two-lane unsigned 16-bit max of packed words (v_pk_max_u16).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+  const v2u16 m = __builtin_elementwise_max(__builtin_bit_cast(v2u16, a), __builtin_bit_cast(v2u16, b));
+  return __builtin_bit_cast(uint32_t, m);
+}
+
+// Packed |x| maxima (two 16-bit lanes) of the regular columns of a chunk.
+__device__ __forceinline__ uint32_t chunk_absmax2(const uint4& w, uint32_t ob) {
+  uint32_t d0 = w.x & 0x7fff7fffu, d1 = w.y & 0x7fff7fffu;
+  uint32_t d2 = w.z & 0x7fff7fffu, d3 = w.w & 0x7fff7fffu;
+  if (ob) {
+    d0 &= keep_halves(ob & 3u);
+    d1 &= keep_halves((ob >> 2) & 3u);
+    d2 &= keep_halves((ob >> 4) & 3u);
+    d3 &= keep_halves((ob >> 6) & 3u);
+  }
+  return pk_max_u16(pk_max_u16(d0, d1), pk_max_u16(d2, d3));
+}
+
+__device__ __forceinline__ uint2 pack8_i8(const int (&q)[8]) {
+  const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)q[1], (uint32_t)q[0], 0x0c0c0400u);
+  const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)q[3], (uint32_t)q[2], 0x0c0c0400u);
+  const uint32_t p45 = __builtin_amdgcn_perm((uint32_t)q[5], (uint32_t)q[4], 0x0c0c0400u);
+  const uint32_t p67 = __builtin_amdgcn_perm((uint32_t)q[7], (uint32_t)q[6], 0x0c0c0400u);
+  return uint2{__builtin_amdgcn_perm(p23, p01, 0x05040100u),
+               __builtin_amdgcn_perm(p67, p45, 0x05040100u)};
+}
+
+// Codes of the 8 columns of a chunk against the row scale a, with
+// r = RN(127/a) (0 when a == 0).  For |x| <= a the exact product x*r lies
+// within 2^-17 of the exact 127x/a, so t = rint(RN(x*r)) is the exact
+// round-half-even code wherever |x*r - t| (one fma) is at most 1/2 - 2^-14;
+// there it also equals rint of the IEEE quotient fp32(127x)/a (checked on
+// every binary16 pair 0 <= x <= a on the host).  Returns the largest such
+// deviation in *dev: above kTieGuard (about 1.5e-4 of the values) the caller
+// recomputes the chunk with quant8_exact.  Outlier columns (|x| > a) get
+// arbitrary codes here; the caller zeroes them.  Branch-free, so the chunks
+// of a row interleave.
+__device__ __forceinline__ uint2 quant8_fast(const uint4& w, float r, float* dev) {
   int q[8];
+  float d = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int v = quant_code(h2f(h[i]), a);  // computed for every column, then selected
-    q[i] = ((ob >> i) & 1u) ? 0 : v;
+    const float x = h2f((uint16_t)half_at(w, i));
+    // RN(x*r) as an fma with a +0 addend, so it reads the binary16 operand
+    // directly (a -0 product becomes +0, which quantizes the same)
+    const float t = rintf(__builtin_fmaf(x, r, 0.0f));
+    d = fmaxf(d, fabsf(__builtin_fmaf(x, r, -t)));
+    q[i] = (int)t;
   }
-  uint2 out;
-  out.x = (uint32_t)pack4_i8(q[0], q[1], q[2], q[3]);
-  out.y = (uint32_t)pack4_i8(q[4], q[5], q[6], q[7]);
-  *reinterpret_cast<uint2*>(Xq + tiled_offset(m, (size_t)c * 8, ldk)) = out;
-  if (ob && XO != nullptr) {
+  *dev = d;
+  return pack8_i8(q);
+}
+
+// The same codes through the IEEE division (quant_code).
+__device__ __forceinline__ uint2 quant8_exact(const uint4& w, float a) {
+  int q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = quant_code(h2f((uint16_t)half_at(w, i)), a);
+  return pack8_i8(q);
+}
+
+// Outlier columns of one chunk of row m (mask bits ob = (word >> sh) & 0xff,
+// ob != 0): their codes zeroed, their values copied to the outlier slice at
+// slots pre + (set bits of word below sh), ...
+__device__ __forceinline__ void outlier_chunk(uint2& q, const uint4& w, int m, uint32_t word,
+                                              int sh, int pre, int ldk,
+                                              uint16_t* __restrict__ XO) {
+  const uint32_t ob = (word >> sh) & 0xffu;
+  q.x &= keep_bytes(ob & 0xfu);
+  q.y &= keep_bytes(ob >> 4);
+  if (XO != nullptr) {
     int slot = pre + __popc(word & ((1u << sh) - 1u));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if ((ob >> i) & 1u) {
-        XO[tiled_offset(m, (size_t)slot * 2, (size_t)ldk * 2) / 2] = h[i];
+        XO[tiled_offset(m, (size_t)slot * 2, (size_t)ldk * 2) / 2] = (uint16_t)half_at(w, i);
         ++slot;
       }
   }
 }
 
+// Codes of one chunk with both fix-ups (the form used when a row is streamed
+// chunk by chunk).
+__device__ __forceinline__ uint2 code_chunk(const uint4& w, int m, uint32_t word, int sh, int pre,
+                                            float r, float a, int ldk,
+                                            uint16_t* __restrict__ XO) {
+  float dev;
+  uint2 q = quant8_fast(w, r, &dev);
+  if (dev > kTieGuard) q = quant8_exact(w, a);
+  if ((word >> sh) & 0xffu) outlier_chunk(q, w, m, word, sh, pre, ldk, XO);
+  return q;
+}
+
+// s_waitcnt vmcnt(0), other counters left alone.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 }  // namespace
+
+// Chunks rl, rl + LPR, ... of one row into registers, zeros from chunk nck
+// = K/8 on; the row is 16-byte aligned and K % 8 == 0 (the register-resident
+// form is used only then).
+template <int CPL, int LPR>
+__device__ __forceinline__ void load_row(uint4 (&h)[CPL > 0 ? CPL : 1], const uint16_t* row, int rl,
+                                         int nck) {
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const int c = rl + u * LPR;
+    h[u] = c < nck ? reinterpret_cast<const uint4*>(row)[c] : uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Keep-masks of the chunks of lane rl (all ones on regular columns, zero on
+// the binary16 halves of outlier columns): the same for every row, so they
+// are built once per block.
+template <int CPL, int LPR>
+__device__ __forceinline__ void chunk_keep_masks(uint4 (&keep)[CPL > 0 ? CPL : 1],
+                                                 const uint32_t* s_bits, int rl, int nch) {
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const int c = rl + u * LPR;
+    const uint32_t ob = c < nch ? (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u;
+    keep[u] = uint4{keep_halves(ob & 3u), keep_halves((ob >> 2) & 3u),
+                    keep_halves((ob >> 4) & 3u), keep_halves((ob >> 6) & 3u)};
+  }
+}
+
+// A lane's entries j = rl, rl + LPR, ... of one row's outlier slice
+// (X_O[m][j] = X[m][O_j] for j < |O|, 0 up to opad), held between their
+// loads and stores.
+struct OutlierRow {
+  uint16_t v[4];
+};
+
+// One row m (< M) held in registers (CPL > 0): outlier columns zeroed by the
+// keep-masks, absmax of |x| (the regular columns), codes, stores.  With
+// WPR == 4 the block's four waves share the row (block barriers inside).
+template <int WPR, int CPL>
+__device__ __forceinline__ void quant_row_regs(uint4 (&h)[CPL > 0 ? CPL : 1],
+                                               const uint4 (&keep)[CPL > 0 ? CPL : 1],
+                                               const uint16_t* __restrict__ X, int m, int K,
+                                               int ldk, int rl, int nch, int total, int opad,
+                                               const uint32_t* s_bits, const int* s_pre,
+                                               const int* s_olist, bool olist_in_lds, int nw,
+                                               uint32_t* s_red, int8_t* __restrict__ Xq,
+                                               float* __restrict__ x_scale,
+                                               uint16_t* __restrict__ XO) {
+  constexpr int LPR = 64 * WPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint16_t* row = X + (size_t)m * K;
+  uint32_t mx2 = 0;  // two packed 16-bit maxima of |x| bits
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    h[u].x &= keep[u].x; h[u].y &= keep[u].y; h[u].z &= keep[u].z; h[u].w &= keep[u].w;
+    mx2 = pk_max_u16(mx2, pk_max_u16(pk_max_u16(h[u].x & 0x7fff7fffu, h[u].y & 0x7fff7fffu),
+                                     pk_max_u16(h[u].z & 0x7fff7fffu, h[u].w & 0x7fff7fffu)));
+  }
+  uint32_t mx = wave_max(max(mx2 & 0xffffu, mx2 >> 16));
+  if (WPR > 1) {
+    __syncthreads();  // s_red of the previous row has been read
+    if (lane == 0) s_red[wave] = mx;
+    __syncthreads();
+    mx = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+  }
+  const float a = h2f((uint16_t)mx);
+  const float r = a == 0.0f ? 0.0f : 127.0f / a;
+  // codes: every chunk straight through (outlier columns hold +-0 -> code 0),
+  // then the chunks with a value near a half-integer again, exactly
+  uint2 q[CPL > 0 ? CPL : 1];
+  uint32_t slow = 0;
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    float dev;
+    q[u] = quant8_fast(h[u], r, &dev);
+    slow |= dev > kTieGuard ? (1u << u) : 0u;
+  }
+  if (slow) {
+#pragma unroll
+    for (int u = 0; u < CPL; ++u)
+      if ((slow >> u) & 1u) q[u] = quant8_exact(h[u], a);
+  }
+  // outlier slice values (loads from the row just read: cache hits)
+  constexpr int kXoPer = 4;  // slice entries per lane and pass
+  OutlierRow xo{{0, 0, 0, 0}};
+  const bool xo_one_pass = opad <= kXoPer * LPR;
+  if (XO != nullptr && xo_one_pass) {
+#pragma unroll
+    for (int p = 0; p < kXoPer; ++p) {
+      const int j = rl + p * LPR;
+      if (j < total) {
+        const int k = olist_in_lds ? s_olist[j] : select_outlier(s_bits, s_pre, nw, j);
+        xo.v[p] = row[k];
+      }
+    }
+  }
+  // Loads and stores share the vector memory counter; with both in flight
+  // the compiler cannot count and waits for all of them at the next use of
+  // a load.  One explicit wait here, after the arithmetic, then the stores.
+  wait_vmem_all();
+  // chunk c = rl + u*LPR starts at byte 8c of the row: LPR*8/64 column
+  // blocks (of kTileBytes each) after chunk rl
+  int8_t* xq_lane = Xq + tiled_offset(m, (size_t)rl * 8, ldk);
+  constexpr size_t kStep = (size_t)LPR * 8 / kTileK * kTileBytes;
+#pragma unroll
+  for (int u = 0; u < CPL; ++u)
+    if (rl + u * LPR < nch) *reinterpret_cast<uint2*>(xq_lane + u * kStep) = q[u];
+  if (XO != nullptr) {
+    if (xo_one_pass) {
+#pragma unroll
+      for (int p = 0; p < kXoPer; ++p) {
+        const int j = rl + p * LPR;
+        if (j < opad) XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = xo.v[p];
+      }
+    } else {
+      for (int j = rl; j < opad; j += LPR) {
+        uint16_t v = 0;
+        if (j < total) v = row[olist_in_lds ? s_olist[j] : select_outlier(s_bits, s_pre, nw, j)];
+        XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = v;
+      }
+    }
+  }
+  if (rl == 0) x_scale[m] = a;
+}
+
+// One row m (< M) streamed from memory twice (CPL == 0: long rows, or rows
+// that are not 16-byte aligned).
+template <int WPR>
+__device__ __forceinline__ void quant_row_stream(const uint16_t* __restrict__ X, int m, int K,
+                                                 int ldk, int vec, int rl, int nch, int total,
+                                                 int opad, const uint32_t* s_bits,
+                                                 const int* s_pre, uint32_t* s_red,
+                                                 int8_t* __restrict__ Xq,
+                                                 float* __restrict__ x_scale,
+                                                 uint16_t* __restrict__ XO) {
+  constexpr int LPR = 64 * WPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint16_t* row = X + (size_t)m * K;
+  uint32_t mx2 = 0;
+  for (int c = rl; c < nch; c += LPR) {
+    const uint4 g = load_chunk(row, c * 8, K, vec != 0);
+    const uint32_t ob = (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu;
+    mx2 = pk_max_u16(mx2, chunk_absmax2(g, ob));
+  }
+  uint32_t mx = wave_max(max(mx2 & 0xffffu, mx2 >> 16));
+  if (WPR > 1) {
+    __syncthreads();
+    if (lane == 0) s_red[wave] = mx;
+    __syncthreads();
+    mx = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+  }
+  const float a = h2f((uint16_t)mx);
+  const float r = a == 0.0f ? 0.0f : 127.0f / a;
+  int8_t* xq_lane = Xq + tiled_offset(m, (size_t)rl * 8, ldk);
+  constexpr size_t kStep = (size_t)LPR * 8 / kTileK * kTileBytes;
+  int u = 0;
+  for (int c = rl; c < nch; c += LPR, ++u) {
+    const uint4 g = load_chunk(row, c * 8, K, vec != 0);
+    *reinterpret_cast<uint2*>(xq_lane + (size_t)u * kStep) =
+        code_chunk(g, m, s_bits[c >> 2], (c & 3) * 8, s_pre[c >> 2], r, a, ldk, XO);
+  }
+  if (XO != nullptr)
+    for (int j = total + rl; j < opad; j += LPR)
+      XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = 0;
+  if (rl == 0) x_scale[m] = a;
+}
 
 // Row pass.  grid = W_O blocks (16 weight rows each; only when WO !=
 // nullptr) followed by row blocks, so the small gather work overlaps the row
 // work instead of forming a tail.  WPR = waves per row: 1 (a wave per row, 4
-// rows per block) or 4 (the whole block on one row, for few rows).  CPL =
-// 8-column chunks per lane held in registers between the absmax and the
-// quantize passes (0: re-read the row from L1/L2 instead, for long rows).
+// rows per block and pass, the blocks looping over the rows) or 4 (the whole
+// block on one row, for few rows).  CPL = 8-column chunks per lane held in
+// registers between the absmax and the quantize passes (0: re-read the row
+// from L1/L2 instead, for long rows).
 // Dynamic LDS: 2*nw words plus the O list (up to kOListCap entries).
 constexpr int kOListCap = 4096;
 constexpr int kWoRows = 16;
+constexpr int kRowBlocks = 2048;  // row blocks of the one-wave-per-row form
 
 template <int WPR, int CPL>
 __global__ __launch_bounds__(256) void k_quant_rows(
@@ -225,10 +507,35 @@ __global__ __launch_bounds__(256) void k_quant_rows(
   const int nw = ldk / 32;
   uint32_t* s_bits = s_dyn;
   int* s_pre = reinterpret_cast<int*>(s_dyn + nw);
-  const int total = load_mask_prefix(mask_bits, nw, s_bits, s_pre);
-  const int opad = (total + 63) & ~63;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int rb = (int)blockIdx.x - n_wo_blocks;  // row block index (< 0: a W_O block)
+  constexpr int RPB = 4 / WPR;               // rows per block and pass
+  constexpr int LPR = 64 * WPR;              // lanes per row
+  const int rl = (wave % WPR) * 64 + lane;   // lane index within the row
+  const int nch = ldk / 8;
+  const int mstride = ((int)gridDim.x - n_wo_blocks) * RPB;
+  int m = rb * RPB + wave / WPR;
+  // the block's first row is loaded before the mask prefix, so the two
+  // memory latencies overlap
+  uint4 ha[CPL > 0 ? CPL : 1];
+  const int nck = K >> 3;  // whole 8-column chunks of a row (K % 8 == 0 when CPL > 0)
+  if (CPL > 0 && rb >= 0 && m < M) load_row<CPL, LPR>(ha, X + (size_t)m * K, rl, nck);
+  const int total = load_mask_prefix(mask_bits, nw, s_bits, s_pre);
+  const int opad = (total + 63) & ~63;
+  // the O list in LDS when it fits (W_O gather, X_O slice)
+  int* s_olist = reinterpret_cast<int*>(s_dyn + 2 * nw);
+  const bool olist_in_lds = total <= kOListCap;
+  if ((WO != nullptr || XO != nullptr) && olist_in_lds) {
+    for (int w = t; w < nw; w += 256) {
+      uint32_t b = s_bits[w];
+      int slot = s_pre[w];
+      while (b) {
+        s_olist[slot++] = w * 32 + __ffs(b) - 1;
+        b &= b - 1;
+      }
+    }
+  }
+  __syncthreads();
 
   if (rb == 0) {
     if (t == 0 && n_out != nullptr) *n_out = total;
@@ -245,21 +552,9 @@ __global__ __launch_bounds__(256) void k_quant_rows(
   }
 
   if (rb < 0) {
-    // ---- W_O[n][j] for 16 weight rows: the O list in LDS (when it fits),
-    // then one (row, j) item per thread and pass, loads issued together.
-    int* s_olist = reinterpret_cast<int*>(s_dyn + 2 * nw);
-    const bool in_lds = total <= kOListCap;
-    if (in_lds) {
-      for (int w = t; w < nw; w += 256) {
-        uint32_t b = s_bits[w];
-        int slot = s_pre[w];
-        while (b) {
-          s_olist[slot++] = w * 32 + __ffs(b) - 1;
-          b &= b - 1;
-        }
-      }
-    }
-    __syncthreads();
+    // ---- W_O[n][j] for 16 weight rows: one (row, j) item per thread and
+    // pass, loads issued together.
+    const bool in_lds = olist_in_lds;
     const int n0 = blockIdx.x * kWoRows;
     const int nl = t >> 4, jl = t & 15;
     const int n = n0 + nl;
@@ -289,71 +584,19 @@ __global__ __launch_bounds__(256) void k_quant_rows(
     return;
   }
 
-  // ---- rows
-  constexpr int RPB = 4 / WPR;               // rows per block
-  constexpr int LPR = 64 * WPR;              // lanes per row
-  const int m = rb * RPB + wave / WPR;
-  const int rl = (wave % WPR) * 64 + lane;   // lane index within the row
-  const int nch = ldk / 8;
-  const bool active = m < M;
-  const uint16_t* row = X + (size_t)min(m, M - 1) * K;
-  uint16_t h[CPL > 0 ? CPL : 1][8];
-  uint32_t mx = 0;
+  // ---- rows m, m + mstride, ... (one pass for M <= 4 * kRowBlocks)
   if (CPL > 0) {
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int c = rl + u * LPR;
-      if (c < nch) {
-        load8_half(row, c * 8, K, vec != 0, h[u]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[u][i] = 0;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int c = rl + u * LPR;
-      const uint32_t ob = c < nch ? (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (!((ob >> i) & 1u)) mx = max(mx, habs_bits(h[u][i]));
+    uint4 keep[CPL > 0 ? CPL : 1];
+    chunk_keep_masks<CPL, LPR>(keep, s_bits, rl, nch);
+    for (bool first = true; m < M; m += mstride, first = false) {
+      if (!first) load_row<CPL, LPR>(ha, X + (size_t)m * K, rl, nck);
+      quant_row_regs<WPR, CPL>(ha, keep, X, m, K, ldk, rl, nch, total, opad, s_bits, s_pre,
+                               s_olist, olist_in_lds, nw, s_red, Xq, x_scale, XO);
     }
   } else {
-    for (int c = rl; c < nch; c += LPR) {
-      uint16_t g[8];
-      load8_half(row, c * 8, K, vec != 0, g);
-      const uint32_t ob = (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (!((ob >> i) & 1u)) mx = max(mx, habs_bits(g[i]));
-    }
-  }
-  mx = wave_max(mx);
-  if (WPR > 1) {
-    if (lane == 0) s_red[wave] = mx;
-    __syncthreads();
-    mx = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
-  }
-  const float a = h2f((uint16_t)mx);
-  if (active) {
-    if (CPL > 0) {
-#pragma unroll
-      for (int u = 0; u < CPL; ++u) {
-        const int c = rl + u * LPR;
-        if (c < nch)
-          emit_chunk(h[u], m, c, s_bits[c >> 2], (c & 3) * 8, s_pre[c >> 2], a, ldk, Xq, XO);
-      }
-    } else {
-      for (int c = rl; c < nch; c += LPR) {
-        uint16_t g[8];
-        load8_half(row, c * 8, K, vec != 0, g);
-        emit_chunk(g, m, c, s_bits[c >> 2], (c & 3) * 8, s_pre[c >> 2], a, ldk, Xq, XO);
-      }
-    }
-    if (XO != nullptr)
-      for (int j = total + rl; j < opad; j += LPR)
-        XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = 0;
-    if (rl == 0) x_scale[m] = a;
+    for (; m < M; m += mstride)
+      quant_row_stream<WPR>(X, m, K, ldk, vec, rl, nch, total, opad, s_bits, s_pre, s_red, Xq,
+                            x_scale, XO);
   }
 }
 
@@ -398,15 +641,19 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
   const int vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
   const bool few_rows = M <= 256;  // whole block per row keeps the GPU busy
   const int wpr = few_rows ? 4 : 1;
-  const int n_row_blocks = few_rows ? M : (M + 3) / 4;
+  // a wave per row (blocks loop over the rows only beyond 4 * kRowBlocks)
+  const int n_row_blocks = few_rows ? M : min((M + 3) / 4, kRowBlocks);
   const int n_wo_blocks = WO != nullptr ? (N + kWoRows - 1) / kWoRows : 0;
   const size_t lds = (size_t)2 * (ldk / 32) * sizeof(uint32_t) +
-                     (WO != nullptr ? (size_t)kOListCap * sizeof(int) : 0);
+                     (WO != nullptr || XO != nullptr ? (size_t)kOListCap * sizeof(int) : 0);
   dim3 grid(n_row_blocks + n_wo_blocks);
   const int lanes = 64 * wpr;
   const int cpl_needed = (ldk / 8 + lanes - 1) / lanes;
 #define QR(W, C) launch_qr<W, C>(grid, lds, s, X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out, out_idx, Wq, w_scale, N, WO)
-  if (wpr == 4) {
+  // rows held in registers need 16-byte loads (aligned X, K % 8 == 0)
+  if (!vec) {
+    if (wpr == 4) QR(4, 0); else QR(1, 0);
+  } else if (wpr == 4) {
     if (cpl_needed <= 4) QR(4, 4);
     else if (cpl_needed <= 8) QR(4, 8);
     else QR(4, 0);

@@ -132,13 +132,13 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
 
   uint16_t* Y = out.C ? nullptr : out.Y;
   if (out.C == nullptr && Y == nullptr) return INT8MM_OK;
-  if (ev_start != nullptr && (e = hipEventRecord(ev_start, s)) != hipSuccess) return hip_fail(e);
   if (L.decode)
-    e = i8mm::launch_gemm_decode(xq, Wq, m, n, k, ldk, xs, w_scale, X, bits, Y, out.C, s);
+    e = i8mm::launch_gemm_decode(xq, Wq, m, n, k, ldk, xs, w_scale, X, bits, Y, out.C, s, ev_start,
+                                 ev_stop);
   else
-    e = i8mm::launch_gemm_prefill(xq, Wq, m, n, ldk, xs, w_scale, xo, wo, count, Y, out.C, s);
+    e = i8mm::launch_gemm_prefill(xq, Wq, m, n, ldk, xs, w_scale, xo, wo, count, Y, out.C, s,
+                                  ev_start, ev_stop);
   if (e != hipSuccess) return hip_fail(e);
-  if (ev_stop != nullptr && (e = hipEventRecord(ev_stop, s)) != hipSuccess) return hip_fail(e);
   return INT8MM_OK;
 }
 

@@ -174,20 +174,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
 }
 
 template <int G>
-static void launch_g(dim3 grid, hipStream_t s, const int8_t* Xq, const int8_t* Wq, int M, int N,
+static void launch_g(dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const int8_t* Xq, const int8_t* Wq, int M, int N,
                      int K, int ldk, const float* xs, const float* ws, const uint16_t* X,
                      const uint32_t* mb, uint16_t* Y, int32_t* C) {
   if (C != nullptr)
-    hipLaunchKernelGGL((k_gemm_decode<G, 1>), grid, dim3(kThreads), 0, s, Xq, Wq, M, N, K, ldk,
-                       xs, ws, X, mb, Y, C);
+    hipExtLaunchKernelGGL((k_gemm_decode<G, 1>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq, Wq, M,
+                          N, K, ldk, xs, ws, X, mb, Y, C);
   else
-    hipLaunchKernelGGL((k_gemm_decode<G, 0>), grid, dim3(kThreads), 0, s, Xq, Wq, M, N, K, ldk,
-                       xs, ws, X, mb, Y, C);
+    hipExtLaunchKernelGGL((k_gemm_decode<G, 0>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq, Wq, M,
+                          N, K, ldk, xs, ws, X, mb, Y, C);
 }
 
 hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                               const float* x_scale, const float* w_scale, const uint16_t* X,
-                              const uint32_t* mask_bits, uint16_t* Y, int32_t* C, hipStream_t s) {
+                              const uint32_t* mask_bits, uint16_t* Y, int32_t* C, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1) {
   // Spread the 16-row groups evenly over the 256 CUs: G groups per workgroup.
   const int groups = (N + 15) / 16;
   int G = (groups + 255) / 256;
@@ -195,14 +196,14 @@ hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, 
   if (G < 1) G = 1;
   dim3 grid((groups + G - 1) / G);
   switch (G) {
-    case 1: launch_g<1>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 2: launch_g<2>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 3: launch_g<3>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 4: launch_g<4>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 5: launch_g<5>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 6: launch_g<6>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 7: launch_g<7>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    default: launch_g<8>(grid, s, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 1: launch_g<1>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 2: launch_g<2>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 3: launch_g<3>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 4: launch_g<4>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 5: launch_g<5>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 6: launch_g<6>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 7: launch_g<7>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    default: launch_g<8>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
   }
   return hipGetLastError();
 }

@@ -488,14 +488,14 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
-                               hipStream_t s) {
+                               hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (C != nullptr)
-    hipLaunchKernelGGL(k_gemm_prefill<1>, dim3(tiles), dim3(NT), 0, s, Xq, Wq, M, N, ldk, x_scale,
-                       w_scale, XO, WO, n_out, Y, C);
+    hipExtLaunchKernelGGL(k_gemm_prefill<1>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
+                          ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
   else
-    hipLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles), dim3(NT), 0, s, Xq, Wq, M, N, ldk, x_scale,
-                       w_scale, XO, WO, n_out, Y, C);
+    hipExtLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
+                          ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
   return hipGetLastError();
 }
 

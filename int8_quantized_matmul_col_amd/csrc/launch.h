@@ -3,6 +3,7 @@
 // launch.  Shapes are validated by the caller (api.hip) before any launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,11 +34,14 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
-                               hipStream_t s);
+                               hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// e0/e1 (optional) are stamped by the GEMM dispatch itself: start and end of
+// that kernel, for profiling.
 // Decode (M <= 16): one streaming pass over Wq, outliers handled inline.
 hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                               const float* x_scale, const float* w_scale, const uint16_t* X,
-                              const uint32_t* mask_bits, uint16_t* Y, int32_t* C, hipStream_t s);
+                              const uint32_t* mask_bits, uint16_t* Y, int32_t* C, hipStream_t s,
+                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // Y[0 .. count) = 0 (K == 0 case).
 hipError_t launch_zero_half(uint16_t* Y, int64_t count, hipStream_t s);
 

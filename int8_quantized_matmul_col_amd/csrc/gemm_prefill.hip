@@ -9,11 +9,15 @@
 // One workgroup = 256x256 output tile, 4 waves in a 2x2 arrangement, each
 // wave a 128x128 block held as 4x4 v_mfma_i32_32x32x32_i8 accumulators
 // (256 AGPRs).  Operands are panel-tiled in memory (tile_layout.h), so one
-// 64-byte K step of a 256-row panel is 16 KiB contiguous: every wave load
-// instruction moves 1 KiB of whole cache lines straight into LDS
-// (global_load_lds_dwordx4: no VGPR staging, no ds_write).  Four LDS stages
-// let loads run two steps ahead and let the first fragments of step k+1 be
-// read before the barrier that ends step k; one barrier per step.
+// 64-byte K step of a 256-row panel is 16 KiB contiguous: each wave load
+// instruction reads 1 KiB of whole cache lines.  Loads go to registers (three
+// rotating one-step buffers, so a load has two steps to land) and from there
+// to LDS with swizzled ds_write_b128: on gfx950 the direct-to-LDS form of a
+// 16-byte load holds up the issuing wave for tens of cycles, which here would
+// stall the MFMA stream; register loads and LDS writes interleave with it for
+// free.  Five LDS stages: the one computed, the next one (its first fragments
+// are read before the barrier ending the current step), the one being
+// written, and two that stay free for the epilogue.  One barrier per step.
 //
 // The outlier slice (|O| rounded up to 32 fp16 columns: 64 bytes per row per
 // step, the same byte shape as an int8 step) is appended to the same
@@ -37,13 +41,11 @@ namespace {
 constexpr int BM = kPanelRows;  // 256
 constexpr int BN = kPanelRows;
 constexpr int NT = 256;
-constexpr int NBUF = 4;  // LDS stages of 256 rows x 64 bytes per operand
+constexpr int NBUF = 5;  // LDS stages of 256 rows x 64 bytes per operand (160 KiB)
 
 struct Smem {
   v4i a[NBUF][BM * 4];
   v4i b[NBUF][BN * 4];
-  float sx[BM];
-  float sw[BN];
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -64,12 +66,34 @@ struct Src {
   int nk8;  // number of int8 steps
 };
 
-// Issue the loads of step s into stage `buf`: 4 instructions per operand per
-// wave, each 64 lanes x 16 bytes = a 1 KiB slice of the 16 KiB block.
-__device__ __forceinline__ void gload(Smem& sm, int buf, const Src& src, int s, int wave,
-                                      int lane) {
-  const char* a;
-  const char* b;
+// One step's loads of one wave, in registers: 4 quads per operand.
+struct Stage8 {
+  v4i a[4];
+  v4i b[4];
+};
+
+// Per-lane constants of the load path.  Load instruction i of wave w reads
+// the 1 KiB at byte (4i + w)*1024 of the step block (lane l: 16 bytes at
+// +16l), i.e. LDS slot q = (4i + w)*64 + l, which it writes to the swizzled
+// position swz(q / 4, q % 4).
+struct LoadMap {
+  uint32_t goff[4];  // byte offset in the step block
+  int lidx[4];       // v4i index in an LDS stage
+};
+
+__device__ __forceinline__ LoadMap load_map(int wave, int lane) {
+  LoadMap mp;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (i * 4 + wave) * 64 + lane;
+    mp.goff[i] = (uint32_t)q * 16;
+    mp.lidx[i] = swz(q >> 2, q & 3);
+  }
+  return mp;
+}
+
+// Block addresses of step s (clamped to the last step by the caller).
+__device__ __forceinline__ void step_src(const Src& src, int s, const char*& a, const char*& b) {
   if (s < src.nk8) {
     a = src.A + (size_t)s * kTileBytes;
     b = src.B + (size_t)s * kTileBytes;
@@ -77,16 +101,39 @@ __device__ __forceinline__ void gload(Smem& sm, int buf, const Src& src, int s, 
     a = src.AO + (size_t)(s - src.nk8) * kTileBytes;
     b = src.BO + (size_t)(s - src.nk8) * kTileBytes;
   }
+}
+
+// Load instruction n (0..7: quad n/2 of operand n%2) of a step into r.
+__device__ __forceinline__ void gload1(Stage8& r, const char* a, const char* b, int n,
+                                       const LoadMap& mp) {
+  const int i = n >> 1;
+  if (n & 1)
+    r.b[i] = *reinterpret_cast<const v4i*>(b + mp.goff[i]);
+  else
+    r.a[i] = *reinterpret_cast<const v4i*>(a + mp.goff[i]);
+}
+
+__device__ __forceinline__ void gload_all(Stage8& r, const Src& src, int s, const LoadMap& mp) {
+  const char* a;
+  const char* b;
+  step_src(src, s, a, b);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s0 = (i * 4 + wave) * 64;
-    const int slot = s0 + lane;
-    const int row = slot >> 2;
-    const int ch = (slot & 3) ^ ((row >> 2) & 3);
-    const int off = row * 64 + ch * 16;
-    __builtin_amdgcn_global_load_lds((const void*)(a + off), (lds_ptr_t)&sm.a[buf][s0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(b + off), (lds_ptr_t)&sm.b[buf][s0], 16, 0, 0);
-  }
+  for (int n = 0; n < 8; ++n) gload1(r, a, b, n, mp);
+}
+
+// LDS write n (0..7) of a step's registers into stage buf.
+__device__ __forceinline__ void lwrite1(Smem& sm, int buf, const Stage8& r, int n,
+                                       const LoadMap& mp) {
+  const int i = n >> 1;
+  if (n & 1)
+    sm.b[buf][mp.lidx[i]] = r.b[i];
+  else
+    sm.a[buf][mp.lidx[i]] = r.a[i];
+}
+
+__device__ __forceinline__ void lwrite_all(Smem& sm, int buf, const Stage8& r, const LoadMap& mp) {
+#pragma unroll
+  for (int n = 0; n < 8; ++n) lwrite1(sm, buf, r, n, mp);
 }
 
 // MFMA operand fragments of one 32-byte K sub-step for the wave's 4x4 tiles.
@@ -123,48 +170,128 @@ __device__ __forceinline__ void mma(const Frag& f, v16i (&acc)[4][4]) {
     }
 }
 
-// s_waitcnt: vmcnt <= 8 (the loads issued in the current step may stay in
-// flight) and lgkmcnt 0; or everything.
-__device__ __forceinline__ void wait_prev_step() {
-  __builtin_amdgcn_s_waitcnt((8 & 0xf) | (7 << 4) | (0 << 8) | ((8 >> 4) << 14));
-}
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-// One pipeline step: fragments of sub-step 1 while sub-step 0 computes, the
-// next step's sub-step-0 fragments while sub-step 1 computes, the loads of
-// step kt+3; then wait for the loads of step kt+2 and this wave's LDS reads,
-// and the barrier.  Branch-free: loads past the end are clamped to the last
-// step (in bounds, landing in a stage that is not read again).
+// One MFMA of tile (i, j) on fragment pair (a, b).
+template <bool F16>
+__device__ __forceinline__ void mma1(v16i& acc, const v4i& a, const v4i& b) {
+  if constexpr (F16) {
+    // acc holds fp32 bit patterns here (reinterpreted in place)
+    acc = __builtin_bit_cast(
+        v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
+                                                     __builtin_bit_cast(v8h, b),
+                                                     __builtin_bit_cast(v16f, acc), 0, 0, 0));
+  } else {
+    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc, 0, 0, 0);
+  }
+}
+
+// One pipeline step kt, in a fixed instruction order (scheduling barriers
+// keep the compiler from regrouping it): 8 groups of 4 MFMAs, groups 0-3 on
+// the sub-step-0 fragments f0 (row tile i = group), groups 4-7 on sub-step 1.
+// Each group also issues 2 fragment reads and 1 global load: groups 0-3 read
+// sub-step 1 of this step into f1 (B fragments first, needed from group 4
+// on), groups 4-7 sub-step 0 of the next step into f0 (free after group 3);
+// the 8 loads fetch step kt+4 into rl.  Groups 0-3 also write step kt+2
+// (registers rw, loaded during step kt-2) into its stage, 2 quads each, so
+// the writes are long done when the step ends.  Then the barrier.  Branch-free: loads past
+// the last step are clamped to it (in bounds, written to stages of steps
+// past the last, which are not read again).
 template <bool F16>
 __device__ __forceinline__ void step(Smem& sm, v16i (&acc)[4][4], Frag& f0, Frag& f1,
-                                     const Src& src, int kt, int last, int wm0, int wn0, int wave,
-                                     int lane) {
-  const int cur = kt & 3, nxt = (kt + 1) & 3, far = (kt + 3) & 3;
-  fload(f1, sm, cur, 1, wm0, wn0, lane);
-  mma<F16>(f0, acc);
-  fload(f0, sm, nxt, 0, wm0, wn0, lane);
-  mma<F16>(f1, acc);
-  gload(sm, far, src, min(kt + 3, last), wave, lane);
-  // sub-step-1 reads over the first 8 MFMAs, prefetch reads over the third
-  // group of 8, the 8 global loads over the last 8 MFMAs
+                                     Stage8& rl, const Stage8& rw, const Src& src, int kt,
+                                     int last, int wm0, int wn0, const LoadMap& mp, int lane) {
+  const int cur = kt % NBUF, nxt = (kt + 1) % NBUF, wst = (kt + 2) % NBUF;
+  const char* ga;
+  const char* gb;
+  step_src(src, min(kt + 4, last), ga, gb);
+  const int r = lane & 31;
+  const int ch1 = 2 + (lane >> 5);  // sub-step 1 chunk
+  const int ch0 = (lane >> 5);      // sub-step 0 chunk
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  for (int g = 0; g < 8; ++g) {
+    const int i = g & 3;
+    Frag& fm = g < 4 ? f0 : f1;  // operands of this group's MFMAs
+    Frag& fr = g < 4 ? f1 : f0;  // fragments read in this group
+    const int rbuf = g < 4 ? cur : nxt;
+    const int rch = g < 4 ? ch1 : ch0;
+    // fragment order over the four groups: b0 b1 | b2 b3 | a0 a1 | a2 a3
+    const int p0 = (g & 3) * 2;
+    v4i* dst0 = p0 < 4 ? &fr.b[p0] : &fr.a[p0 - 4];
+    v4i* dst1 = p0 < 4 ? &fr.b[p0 + 1] : &fr.a[p0 - 3];
+    const int row0 = p0 < 4 ? wn0 + p0 * 32 + r : wm0 + (p0 - 4) * 32 + r;
+    const int row1 = row0 + 32;
+    mma1<F16>(acc[i][0], fm.a[i], fm.b[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    *dst0 = p0 < 4 ? sm.b[rbuf][swz(row0, rch)] : sm.a[rbuf][swz(row0, rch)];
+    __builtin_amdgcn_sched_barrier(0);
+    mma1<F16>(acc[i][1], fm.a[i], fm.b[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    *dst1 = p0 < 4 ? sm.b[rbuf][swz(row1, rch)] : sm.a[rbuf][swz(row1, rch)];
+    __builtin_amdgcn_sched_barrier(0);
+    mma1<F16>(acc[i][2], fm.a[i], fm.b[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    gload1(rl, ga, gb, g, mp);
+    __builtin_amdgcn_sched_barrier(0);
+    mma1<F16>(acc[i][3], fm.a[i], fm.b[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g < 4) {
+      lwrite1(sm, wst, rw, 2 * g, mp);
+      lwrite1(sm, wst, rw, 2 * g + 1, mp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-  }
-  wait_prev_step();
+  // LDS operations complete in order: lgkmcnt(2) leaves only the last two
+  // fragment reads (needed from group 2 of the next step on) in flight, so
+  // this wave's writes of stage kt+2 have landed before the barrier
+  __builtin_amdgcn_s_waitcnt(0xc27f);
   __builtin_amdgcn_s_barrier();
+}
+
+// Steps kt of [k0, k1) in order; the register buffers rotate with kt mod 3
+// (step kt loads step kt+4 into buf[(kt+1)%3] and writes step kt+2 from
+// buf[(kt+2)%3]).  Unrolled by three so that the roles are static.
+template <bool F16>
+__device__ __forceinline__ void run_steps(Smem& sm, v16i (&acc)[4][4], Frag& f0, Frag& f1,
+                                          Stage8& b0, Stage8& b1, Stage8& b2, const Src& src,
+                                          int k0, int k1, int last, int wm0, int wn0,
+                                          const LoadMap& mp, int lane) {
+  int kt = k0;
+  // bring kt to a multiple of 3
+  while (kt < k1 && kt % 3 != 0) {
+    if (kt % 3 == 1)
+      step<F16>(sm, acc, f0, f1, b2, b0, src, kt, last, wm0, wn0, mp, lane);
+    else
+      step<F16>(sm, acc, f0, f1, b0, b1, src, kt, last, wm0, wn0, mp, lane);
+    ++kt;
+  }
+  for (; kt + 3 <= k1; kt += 3) {
+    step<F16>(sm, acc, f0, f1, b1, b2, src, kt, last, wm0, wn0, mp, lane);
+    step<F16>(sm, acc, f0, f1, b2, b0, src, kt + 1, last, wm0, wn0, mp, lane);
+    step<F16>(sm, acc, f0, f1, b0, b1, src, kt + 2, last, wm0, wn0, mp, lane);
+  }
+  if (kt < k1) {
+    step<F16>(sm, acc, f0, f1, b1, b2, src, kt, last, wm0, wn0, mp, lane);
+    ++kt;
+  }
+  if (kt < k1) step<F16>(sm, acc, f0, f1, b2, b0, src, kt, last, wm0, wn0, mp, lane);
+}
+
+// Pipeline prologue: steps 0 and 1 into stages 0 and 1 (through buffers 0
+// and 1), then the loads of steps 2 and 3 into buffers 2 and 0, the first
+// fragments of step 0.
+__device__ __forceinline__ void prologue(Smem& sm, Frag& f0, Stage8& b0, Stage8& b1, Stage8& b2,
+                                         const Src& src, int last, int wm0, int wn0,
+                                         const LoadMap& mp, int lane) {
+  gload_all(b0, src, 0, mp);
+  gload_all(b1, src, min(1, last), mp);
+  lwrite_all(sm, 0, b0, mp);
+  lwrite_all(sm, 1, b1, mp);
+  gload_all(b2, src, min(2, last), mp);
+  gload_all(b0, src, min(3, last), mp);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  fload(f0, sm, 0, 0, wm0, wn0, lane);
 }
 
 // Row (within the wave block) of accumulator element r of lane `lane` for a
@@ -218,18 +345,13 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
   src.BO = (const char*)WO + (size_t)tn * (2 * nk8) * kTileBytes;
   src.nk8 = nk8;
 
-  // prologue: stages 0..2
-  gload(sm, 0, src, 0, wave, lane);
-  gload(sm, 1, src, min(1, last), wave, lane);
-  gload(sm, 2, src, min(2, last), wave, lane);
-  wait_all();
-  __builtin_amdgcn_s_barrier();
+  const LoadMap mp = load_map(__builtin_amdgcn_readfirstlane(wave), lane);
+  Stage8 b0, b1, b2;
   Frag f0, f1;
-  fload(f0, sm, 0, 0, wm0, wn0, lane);
+  prologue(sm, f0, b0, b1, b2, src, last, wm0, wn0, mp, lane);
 
   // ---- int8 x int8 -> int32 over all K (outlier columns of Xq are zero)
-  int kt = 0;
-  for (; kt < nk8; ++kt) step<false>(sm, acc, f0, f1, src, kt, last, wm0, wn0, wave, lane);
+  run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nk8, last, wm0, wn0, mp, lane);
 
   if (false) {
     wait_all();
@@ -246,39 +368,27 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
     return;
   }
 
-  // ---- scales of the tile's rows and columns
-  {
-    const int t = threadIdx.x;
-    sm.sx[t] = x_scale[min(m0 + t, M - 1)];
-    sm.sw[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
-  }
   const int n_col = n0 + wn0 + (lane & 15) * 8;
   const bool vec_store = (N & 7) == 0;
 
   // ---- many outlier columns: dequantize in place, fp32(C) * a_x[m] * a_w[n]
-  // / 127^2, and continue the pipeline over the fp16 steps on top.
-  __syncthreads();
+  // / 127^2 (scales read from memory: every LDS stage is still in use), and
+  // continue the pipeline over the fp16 steps on top.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float sx[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const v4f v = *reinterpret_cast<const v4f*>(&sm.sx[wm0 + i * 32 + q * 8 + (lane >> 5) * 4]);
-      sx[q * 4 + 0] = v[0];
-      sx[q * 4 + 1] = v[1];
-      sx[q * 4 + 2] = v[2];
-      sx[q * 4 + 3] = v[3];
-    }
+    for (int r = 0; r < 16; ++r) sx[r] = x_scale[min(m0 + wm0 + i * 32 + acc_row(r, lane), M - 1)];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float sw = sm.sw[wn0 + j * 32 + (lane & 31)];
+      const float sw = w_scale[min(n0 + wn0 + j * 32 + (lane & 31), N - 1)] * kInv127Sq;
       v16f f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) f[r] = (float)acc[i][j][r] * (sx[r] * sw);
       acc[i][j] = __builtin_bit_cast(v16i, f);
     }
   }
-  for (; kt <= last; ++kt) step<true>(sm, acc, f0, f1, src, kt, last, wm0, wn0, wave, lane);
+  run_steps<true>(sm, acc, f0, f1, b0, b1, b2, src, nk8, last + 1, last, wm0, wn0, mp, lane);
 
   // store fp16 Y through LDS: two 64-row halves per wave, 16 KiB each
   wait_all();
@@ -369,18 +479,13 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   src.BO = (const char*)WO + (size_t)tn * (2 * nk8) * kTileBytes;
   src.nk8 = nk8;
 
-  // prologue: stages 0..2
-  gload(sm, 0, src, 0, wave, lane);
-  gload(sm, 1, src, min(1, last), wave, lane);
-  gload(sm, 2, src, min(2, last), wave, lane);
-  wait_all();
-  __builtin_amdgcn_s_barrier();
+  const LoadMap mp = load_map(__builtin_amdgcn_readfirstlane(wave), lane);
+  Stage8 b0, b1, b2;
   Frag f0, f1;
-  fload(f0, sm, 0, 0, wm0, wn0, lane);
+  prologue(sm, f0, b0, b1, b2, src, last, wm0, wn0, mp, lane);
 
   // ---- int8 x int8 -> int32 over all K (outlier columns of Xq are zero)
-  int kt = 0;
-  for (; kt < nk8; ++kt) step<false>(sm, acc, f0, f1, src, kt, last, wm0, wn0, wave, lane);
+  run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nk8, last, wm0, wn0, mp, lane);
 
   if (MODE == 1) {
     wait_all();
@@ -397,25 +502,39 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     return;
   }
 
-  // ---- scales of the tile's rows and columns
-  {
-    const int t = threadIdx.x;
-    sm.sx[t] = x_scale[min(m0 + t, M - 1)];
-    sm.sw[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
-  }
   const int n_col = n0 + wn0 + (lane & 15) * 8;
   const bool vec_store = (N & 7) == 0;
 
   {
-    // Few outlier steps: their operands were prefetched into LDS stages
-    // (nk8 + s) & 3 by the int8 loop.  Per 32-row group i: the outlier
-    // product into a 64-register temporary, then Y = fp32(C)*s + Y_O read
-    // straight from the int32 accumulators, converted to fp16, staged in the
-    // free LDS stage (nk8 + 3) & 3 (8 KiB per wave) and stored as 256-byte
-    // row segments.
+    // Few outlier steps (at most 3): steps nk8 and nk8+1 were written to LDS
+    // stages (nk8 + s) % NBUF by the int8 loop, step nk8+2 is still in
+    // registers (buffer (nk8+2) % 3) and is written here.  Stages
+    // (nk8 + 3) % NBUF and (nk8 + 4) % NBUF held the last two int8 steps,
+    // whose reads ended at the last barriers: the tile's scales go to the
+    // second, fp16 Y is staged in the first (8 KiB per wave).  Per 32-row
+    // group i: Y = fp32(C)*s read straight from the int32 accumulators, the
+    // outlier product accumulated on top, converted to fp16 and stored as
+    // 256-byte row segments.
+    float* s_x = reinterpret_cast<float*>(&sm.a[(nk8 + NBUF - 1) % NBUF][0]);
+    float* s_w = s_x + BM;
+    {
+      const int t = threadIdx.x;
+      s_x[t] = x_scale[min(m0 + t, M - 1)];
+      s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
+    }
     wait_all();
+    {
+      const int w3 = (nk8 + 2) % NBUF;
+      const int rb = (nk8 + 2) % 3;
+      if (rb == 0)
+        lwrite_all(sm, w3, b0, mp);
+      else if (rb == 1)
+        lwrite_all(sm, w3, b1, mp);
+      else
+        lwrite_all(sm, w3, b2, mp);
+    }
     __syncthreads();
-    const int fs = (nk8 + 3) & 3;
+    const int fs = (nk8 + 3) % NBUF;
     uint16_t* ys = reinterpret_cast<uint16_t*>(wave < 2 ? &sm.a[fs][0] : &sm.b[fs][0]) +
                    (wave & 1) * (32 * 128);
 #pragma unroll
@@ -426,7 +545,7 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const v4f v =
-            *reinterpret_cast<const v4f*>(&sm.sx[wm0 + i * 32 + q * 8 + (lane >> 5) * 4]);
+            *reinterpret_cast<const v4f*>(&s_x[wm0 + i * 32 + q * 8 + (lane >> 5) * 4]);
         sx[q * 4 + 0] = v[0];
         sx[q * 4 + 1] = v[1];
         sx[q * 4 + 2] = v[2];
@@ -435,12 +554,12 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
       v16f y[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float sw = sm.sw[wn0 + j * 32 + (lane & 31)];
+        const float sw = s_w[wn0 + j * 32 + (lane & 31)];
 #pragma unroll
         for (int r = 0; r < 16; ++r) y[j][r] = (float)acc[i][j][r] * (sx[r] * sw);
       }
       for (int st = 0; st < nk16; ++st) {
-        const int stg = (nk8 + st) & 3;
+        const int stg = (nk8 + st) % NBUF;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const int ch = kk * 2 + (lane >> 5);

@@ -221,19 +221,19 @@ __device__ __forceinline__ void step(Smem& sm, v16i (&acc)[4][4], Frag& f0, Frag
     v4i* dst1 = p0 < 4 ? &fr.b[p0 + 1] : &fr.a[p0 - 3];
     const int row0 = p0 < 4 ? wn0 + p0 * 32 + r : wm0 + (p0 - 4) * 32 + r;
     const int row1 = row0 + 32;
-    mma1<F16>(acc[i][0], fm.a[i], fm.b[0]);
+    mma1<F16>(acc[i][0], fm.b[0], fm.a[i]);
     __builtin_amdgcn_sched_barrier(0);
     *dst0 = p0 < 4 ? sm.b[rbuf][swz(row0, rch)] : sm.a[rbuf][swz(row0, rch)];
     __builtin_amdgcn_sched_barrier(0);
-    mma1<F16>(acc[i][1], fm.a[i], fm.b[1]);
+    mma1<F16>(acc[i][1], fm.b[1], fm.a[i]);
     __builtin_amdgcn_sched_barrier(0);
     *dst1 = p0 < 4 ? sm.b[rbuf][swz(row1, rch)] : sm.a[rbuf][swz(row1, rch)];
     __builtin_amdgcn_sched_barrier(0);
-    mma1<F16>(acc[i][2], fm.a[i], fm.b[2]);
+    mma1<F16>(acc[i][2], fm.b[2], fm.a[i]);
     __builtin_amdgcn_sched_barrier(0);
     gload1(rl, ga, gb, g, mp);
     __builtin_amdgcn_sched_barrier(0);
-    mma1<F16>(acc[i][3], fm.a[i], fm.b[3]);
+    mma1<F16>(acc[i][3], fm.b[3], fm.a[i]);
     __builtin_amdgcn_sched_barrier(0);
     if (g < 4) {
       lwrite1(sm, wst, rw, 2 * g, mp);
@@ -294,10 +294,61 @@ __device__ __forceinline__ void prologue(Smem& sm, Frag& f0, Stage8& b0, Stage8&
   fload(f0, sm, 0, 0, wm0, wn0, lane);
 }
 
-// Row (within the wave block) of accumulator element r of lane `lane` for a
-// 32x32 MFMA tile: rows 8*(r/4) + 4*(lane/32) + r%4, column lane%32.
-__device__ __forceinline__ int acc_row(int r, int lane) {
+// The MFMAs take the W fragment as their first operand, so accumulator
+// element r of lane `lane` for tile (i, j) holds C at row i*32 + lane%32 and
+// column j*32 + acc_col(r, lane) of the wave block: a lane owns one row and
+// runs of 4 consecutive columns.
+__device__ __forceinline__ int acc_col(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+
+// Stores one 32x128 row group of the wave block (fp32, accumulator layout)
+// as fp16 Y rows m_base .. m_base+31, columns n_col0 + 8*(lane%16) .. +7 per
+// lane on the way out, through the wave's 8 KiB staging area ys: each lane
+// writes its 4-column runs as 8-byte pieces (piece k of row r at position
+// k ^ 2*(r%16): the 32 rows of one write instruction spread over the banks),
+// then reads whole 16-byte row pieces back for 256-byte row-segment stores.
+__device__ __forceinline__ void store_rows(const v16f (&y)[4], uint16_t* ys,
+                                           uint16_t* __restrict__ Y, int M, int N, int m_base,
+                                           int n_col0, bool vec_store, int lane) {
+  const int row = lane & 31;
+  const int sw = 2 * (row & 15);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = j * 8 + q * 2 + (lane >> 5);
+      uint2 v;
+      v.x = (uint32_t)f2h(y[j][4 * q]) | ((uint32_t)f2h(y[j][4 * q + 1]) << 16);
+      v.y = (uint32_t)f2h(y[j][4 * q + 2]) | ((uint32_t)f2h(y[j][4 * q + 3]) << 16);
+      *reinterpret_cast<uint2*>(ys + row * 128 + (k ^ sw) * 4) = v;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int c16 = lane & 15;
+  const int n_col = n_col0 + c16 * 8;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int rl = p * 4 + (lane >> 4);  // row within the 32-row group
+    const int m = m_base + rl;
+    const int pos = (2 * c16) ^ (2 * (rl & 15));  // even: the pair stays in order
+    const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 128 + pos * 4);
+    if (m < M) {
+      if (vec_store && n_col + 8 <= N) {
+        // Y is written once and not read again here: stream it past the caches
+        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col));
+      } else {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 }  // namespace
@@ -361,14 +412,13 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm0 + i * 32 + acc_row(r, lane);
-          const int n = n0 + wn0 + j * 32 + (lane & 31);
+          const int m = m0 + wm0 + i * 32 + (lane & 31);
+          const int n = n0 + wn0 + j * 32 + acc_col(r, lane);
           if (m < M && n < N) C[(size_t)m * N + n] = acc[i][j][r];
         }
     return;
   }
 
-  const int n_col = n0 + wn0 + (lane & 15) * 8;
   const bool vec_store = (N & 7) == 0;
 
   // ---- many outlier columns: dequantize in place, fp32(C) * a_x[m] * a_w[n]
@@ -376,59 +426,30 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
   // continue the pipeline over the fp16 steps on top.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float sx[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sx[r] = x_scale[min(m0 + wm0 + i * 32 + acc_row(r, lane), M - 1)];
+    const float sx = x_scale[min(m0 + wm0 + i * 32 + (lane & 31), M - 1)];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float sw = w_scale[min(n0 + wn0 + j * 32 + (lane & 31), N - 1)] * kInv127Sq;
       v16f f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) f[r] = (float)acc[i][j][r] * (sx[r] * sw);
+      for (int r = 0; r < 16; ++r) {
+        const float sw = w_scale[min(n0 + wn0 + j * 32 + acc_col(r, lane), N - 1)] * kInv127Sq;
+        f[r] = (float)acc[i][j][r] * (sx * sw);
+      }
       acc[i][j] = __builtin_bit_cast(v16i, f);
     }
   }
   run_steps<true>(sm, acc, f0, f1, b0, b1, b2, src, nk8, last + 1, last, wm0, wn0, mp, lane);
 
-  // store fp16 Y through LDS: two 64-row halves per wave, 16 KiB each
+  // store fp16 Y through LDS, 8 KiB per wave
   wait_all();
   __syncthreads();
-  uint16_t* ys = reinterpret_cast<uint16_t*>(&sm.a[0][0]) + wave * (64 * 128);
+  uint16_t* ys = reinterpret_cast<uint16_t*>(&sm.a[0][0]) + wave * (32 * 128);
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int i = 0; i < 4; ++i) {
+    v16f y[4];
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = half * 2 + ii;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v16f f = __builtin_bit_cast(v16f, acc[i][j]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ys[(ii * 32 + acc_row(r, lane)) * 128 + j * 32 + (lane & 31)] = f2h(f[r]);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int rl = p * 4 + (lane >> 4);  // row within the 64-row half
-      const int m = m0 + wm0 + half * 64 + rl;
-      const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 128 + (lane & 15) * 8);
-      if (m < M) {
-        if (vec_store && n_col + 8 <= N) {
-          *reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col) = v;
-        } else {
-          const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int j = 0; j < 4; ++j) y[j] = __builtin_bit_cast(v16f, acc[i][j]);
+    store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
   }
 }
 
@@ -495,14 +516,13 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm0 + i * 32 + acc_row(r, lane);
-          const int n = n0 + wn0 + j * 32 + (lane & 31);
+          const int m = m0 + wm0 + i * 32 + (lane & 31);
+          const int n = n0 + wn0 + j * 32 + acc_col(r, lane);
           if (m < M && n < N) C[(size_t)m * N + n] = acc[i][j][r];
         }
     return;
   }
 
-  const int n_col = n0 + wn0 + (lane & 15) * 8;
   const bool vec_store = (N & 7) == 0;
 
   {
@@ -541,23 +561,16 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     for (int i = 0; i < 4; ++i) {
       // row group i: scaled int8 part first (its accumulator registers are
       // then free for the fp16 MFMAs), outlier products accumulated on top
-      float sx[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const v4f v =
-            *reinterpret_cast<const v4f*>(&s_x[wm0 + i * 32 + q * 8 + (lane >> 5) * 4]);
-        sx[q * 4 + 0] = v[0];
-        sx[q * 4 + 1] = v[1];
-        sx[q * 4 + 2] = v[2];
-        sx[q * 4 + 3] = v[3];
-      }
+      const float sx = s_x[wm0 + i * 32 + (lane & 31)];
       v16f y[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float sw = s_w[wn0 + j * 32 + (lane & 31)];
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) y[j][r] = (float)acc[i][j][r] * (sx[r] * sw);
-      }
+        for (int q = 0; q < 4; ++q) {
+          const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[wn0 + j * 32 + q * 8 + (lane >> 5) * 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]);
+        }
       for (int st = 0; st < nk16; ++st) {
         const int stg = (nk8 + st) % NBUF;
 #pragma unroll
@@ -567,37 +580,11 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const v8h b = __builtin_bit_cast(v8h, sm.b[stg][swz(wn0 + j * 32 + (lane & 31), ch)]);
-            y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, y[j], 0, 0, 0);
+            y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, y[j], 0, 0, 0);
           }
         }
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ys[acc_row(r, lane) * 128 + j * 32 + (lane & 31)] = f2h(y[j][r]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int rl = p * 4 + (lane >> 4);  // row within the 32-row group
-        const int m = m0 + wm0 + i * 32 + rl;
-        const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 128 + (lane & 15) * 8);
-        if (m < M) {
-          if (vec_store && n_col + 8 <= N) {
-            *reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col) = v;
-          } else {
-            const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
-          }
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
     }
     return;
   }

@@ -6,30 +6,32 @@
 // ("LLM.int8() notes", section 2.3: the INT8 term plus the FP16 outlier term;
 // "PyTorch 2.9 supports LLM.int8()", section 3: results merged at the end.)
 //
-// One workgroup = 256x256 output tile, 4 waves in a 2x2 arrangement, each
-// wave a 128x128 block held as 4x4 v_mfma_i32_32x32x32_i8 accumulators
-// (256 AGPRs).  Operands are panel-tiled in memory (tile_layout.h), so one
-// 64-byte K step of a 256-row panel is 16 KiB contiguous: each wave load
-// instruction reads 1 KiB of whole cache lines.  Loads go to registers (three
-// rotating one-step buffers, so a load has two steps to land) and from there
-// to LDS with swizzled ds_write_b128: on gfx950 the direct-to-LDS form of a
-// 16-byte load holds up the issuing wave for tens of cycles, which here would
-// stall the MFMA stream; register loads and LDS writes interleave with it for
-// free.  Five LDS stages: the one computed, the next one (its first fragments
-// are read before the barrier ending the current step), the one being
-// written, and two that stay free for the epilogue.  One barrier per step.
+// One workgroup = 256x256 output tile, 8 waves, two per SIMD, in a 2x4
+// arrangement: each wave owns a 128x64 block held as 4x2
+// v_mfma_i32_32x32x32_i8 accumulators (128 AGPRs).  Two waves per SIMD let
+// one wave's memory and LDS instructions, which hold up the issuing wave,
+// overlap the other wave's MFMAs.  Operands are panel-tiled in memory
+// (tile_layout.h), so one 64-byte K step of a 256-row panel is 16 KiB
+// contiguous: each wave load instruction reads 1 KiB of whole cache lines.
+// Loads go to registers (three rotating one-step buffers, so a load has two
+// steps to land) and from there to LDS with swizzled ds_write_b128.  Five LDS
+// stages: the one computed, the next one (its first fragments are read before
+// the barrier ending the current step), the one being written, and two that
+// stay free for the epilogue.  One barrier per step.
 //
 // The outlier slice (|O| rounded up to 32 fp16 columns: 64 bytes per row per
 // step, the same byte shape as an int8 step) is appended to the same
-// pipeline as extra steps on v_mfma_f32_32x32x16_f16: their loads are issued
-// during the last int8 steps, the int32 accumulators are rescaled to fp32 in
-// place in between, and the fp16 products accumulate on top.  |O| is read on
-// the device: no host synchronisation.
+// pipeline as extra steps on v_mfma_f32_32x32x16_f16.  With at most three
+// such steps their operands are prefetched by the int8 loop and the fp16
+// products are added in the epilogue; with more, the int32 accumulators are
+// rescaled to fp32 in place and the pipeline continues over the fp16 steps
+// (out of line).  |O| is read on the device: no host synchronisation.
 //
 // MFMA operand convention: lane l supplies row (l%32) of its operand and 16
-// bytes of K; A and B fragments use the same K mapping, so the pairing of K
+// bytes of K; both fragments use the same K mapping, so the pairing of K
 // indices is consistent whatever order the hardware assigns inside the 16
-// bytes (exact for the int8 sum, within fp32 rounding for fp16).
+// bytes (exact for the int8 sum, within fp32 rounding for fp16).  The W
+// fragment is the MFMA's first operand, so each lane owns output rows.
 #include "device_common.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -40,21 +42,23 @@ namespace {
 
 constexpr int BM = kPanelRows;  // 256
 constexpr int BN = kPanelRows;
-constexpr int NT = 256;
+constexpr int NW = 8;           // waves per workgroup
+constexpr int NT = 64 * NW;
 constexpr int NBUF = 5;  // LDS stages of 256 rows x 64 bytes per operand (160 KiB)
+constexpr int WM = 128;  // wave block rows (4 MFMA tiles)
+constexpr int WN = 64;   // wave block columns (2 MFMA tiles)
+constexpr int TI = WM / 32;
+constexpr int TJ = WN / 32;
 
 struct Smem {
   v4i a[NBUF][BM * 4];
   v4i b[NBUF][BN * 4];
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // LDS slot of 16-byte chunk `ch` (0..3) of tile row `row`.  gfx950 LDS serves
 // a 16-byte read in groups of 16 lanes (64 banks, 256 B/clk): 16 consecutive
 // rows then hit 16 distinct slots when the chunk is XORed with bits 2..3 of
-// the row.  The direct-to-LDS loads fill 64 consecutive slots per wave
-// instruction, so the swizzle is applied on the global-address side.
+// the row.
 __device__ __forceinline__ int swz(int row, int ch) { return row * 4 + (ch ^ ((row >> 2) & 3)); }
 
 // Source of pipeline step s: int8 steps first, then fp16 outlier steps.
@@ -66,26 +70,25 @@ struct Src {
   int nk8;  // number of int8 steps
 };
 
-// One step's loads of one wave, in registers: 4 quads per operand.
-struct Stage8 {
-  v4i a[4];
-  v4i b[4];
+// One step's loads of one wave, in registers: 2 quads per operand.
+struct Stage4 {
+  v4i v[4];  // n = 2*i + operand
 };
 
-// Per-lane constants of the load path.  Load instruction i of wave w reads
-// the 1 KiB at byte (4i + w)*1024 of the step block (lane l: 16 bytes at
-// +16l), i.e. LDS slot q = (4i + w)*64 + l, which it writes to the swizzled
-// position swz(q / 4, q % 4).
+// Per-lane constants of the load path.  Load instruction n of wave w reads
+// the 1 KiB slice (n/2)*NW + w of the step block of operand n%2 (lane l: 16
+// bytes at +16l), i.e. LDS slot q = slice*64 + l, which it writes to the
+// swizzled position swz(q / 4, q % 4).
 struct LoadMap {
-  uint32_t goff[4];  // byte offset in the step block
-  int lidx[4];       // v4i index in an LDS stage
+  uint32_t goff[2];  // byte offset in the step block, per slice index i
+  int lidx[2];       // v4i index in an LDS stage
 };
 
 __device__ __forceinline__ LoadMap load_map(int wave, int lane) {
   LoadMap mp;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = (i * 4 + wave) * 64 + lane;
+  for (int i = 0; i < 2; ++i) {
+    const int q = (i * NW + wave) * 64 + lane;
     mp.goff[i] = (uint32_t)q * 16;
     mp.lidx[i] = swz(q >> 2, q & 3);
   }
@@ -103,103 +106,81 @@ __device__ __forceinline__ void step_src(const Src& src, int s, const char*& a, 
   }
 }
 
-// Load instruction n (0..7: quad n/2 of operand n%2) of a step into r.
-__device__ __forceinline__ void gload1(Stage8& r, const char* a, const char* b, int n,
+// Load instruction n (0..3) of a step into r.
+__device__ __forceinline__ void gload1(Stage4& r, const char* a, const char* b, int n,
                                        const LoadMap& mp) {
   const int i = n >> 1;
-  if (n & 1)
-    r.b[i] = *reinterpret_cast<const v4i*>(b + mp.goff[i]);
-  else
-    r.a[i] = *reinterpret_cast<const v4i*>(a + mp.goff[i]);
+  r.v[n] = *reinterpret_cast<const v4i*>(((n & 1) ? b : a) + mp.goff[i]);
 }
 
-__device__ __forceinline__ void gload_all(Stage8& r, const Src& src, int s, const LoadMap& mp) {
+__device__ __forceinline__ void gload_all(Stage4& r, const Src& src, int s, const LoadMap& mp) {
   const char* a;
   const char* b;
   step_src(src, s, a, b);
 #pragma unroll
-  for (int n = 0; n < 8; ++n) gload1(r, a, b, n, mp);
+  for (int n = 0; n < 4; ++n) gload1(r, a, b, n, mp);
 }
 
-// LDS write n (0..7) of a step's registers into stage buf.
-__device__ __forceinline__ void lwrite1(Smem& sm, int buf, const Stage8& r, int n,
+// LDS write n (0..3) of a step's registers into stage buf.
+__device__ __forceinline__ void lwrite1(Smem& sm, int buf, const Stage4& r, int n,
                                        const LoadMap& mp) {
   const int i = n >> 1;
   if (n & 1)
-    sm.b[buf][mp.lidx[i]] = r.b[i];
+    sm.b[buf][mp.lidx[i]] = r.v[n];
   else
-    sm.a[buf][mp.lidx[i]] = r.a[i];
+    sm.a[buf][mp.lidx[i]] = r.v[n];
 }
 
-__device__ __forceinline__ void lwrite_all(Smem& sm, int buf, const Stage8& r, const LoadMap& mp) {
+__device__ __forceinline__ void lwrite_all(Smem& sm, int buf, const Stage4& r, const LoadMap& mp) {
 #pragma unroll
-  for (int n = 0; n < 8; ++n) lwrite1(sm, buf, r, n, mp);
+  for (int n = 0; n < 4; ++n) lwrite1(sm, buf, r, n, mp);
 }
 
-// MFMA operand fragments of one 32-byte K sub-step for the wave's 4x4 tiles.
+// MFMA operand fragments of one 32-byte K sub-step for the wave's 4x2 tiles.
 struct Frag {
-  v4i a[4];
-  v4i b[4];
+  v4i a[TI];
+  v4i b[TJ];
 };
 
 __device__ __forceinline__ void fload(Frag& f, const Smem& sm, int buf, int kk, int wm0, int wn0,
                                       int lane) {
   const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = sm.a[buf][swz(wm0 + i * 32 + (lane & 31), ch)];
+  for (int i = 0; i < TI; ++i) f.a[i] = sm.a[buf][swz(wm0 + i * 32 + (lane & 31), ch)];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = sm.b[buf][swz(wn0 + j * 32 + (lane & 31), ch)];
-}
-
-template <bool F16>
-__device__ __forceinline__ void mma(const Frag& f, v16i (&acc)[4][4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (F16) {
-        // acc holds fp32 bit patterns here (reinterpreted in place)
-        acc[i][j] = __builtin_bit_cast(
-            v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, f.a[i]),
-                                                         __builtin_bit_cast(v8h, f.b[j]),
-                                                         __builtin_bit_cast(v16f, acc[i][j]), 0,
-                                                         0, 0));
-      } else {
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-      }
-    }
+  for (int j = 0; j < TJ; ++j) f.b[j] = sm.b[buf][swz(wn0 + j * 32 + (lane & 31), ch)];
 }
 
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-// One MFMA of tile (i, j) on fragment pair (a, b).
+// One MFMA on fragment pair (w, x): the W fragment first.
 template <bool F16>
-__device__ __forceinline__ void mma1(v16i& acc, const v4i& a, const v4i& b) {
+__device__ __forceinline__ void mma1(v16i& acc, const v4i& w, const v4i& x) {
   if constexpr (F16) {
     // acc holds fp32 bit patterns here (reinterpreted in place)
     acc = __builtin_bit_cast(
-        v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
-                                                     __builtin_bit_cast(v8h, b),
+        v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, w),
+                                                     __builtin_bit_cast(v8h, x),
                                                      __builtin_bit_cast(v16f, acc), 0, 0, 0));
   } else {
-    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(w, x, acc, 0, 0, 0);
   }
 }
 
 // One pipeline step kt, in a fixed instruction order (scheduling barriers
-// keep the compiler from regrouping it): 8 groups of 4 MFMAs, groups 0-3 on
-// the sub-step-0 fragments f0 (row tile i = group), groups 4-7 on sub-step 1.
-// Each group also issues 2 fragment reads and 1 global load: groups 0-3 read
-// sub-step 1 of this step into f1 (B fragments first, needed from group 4
-// on), groups 4-7 sub-step 0 of the next step into f0 (free after group 3);
-// the 8 loads fetch step kt+4 into rl.  Groups 0-3 also write step kt+2
-// (registers rw, loaded during step kt-2) into its stage, 2 quads each, so
-// the writes are long done when the step ends.  Then the barrier.  Branch-free: loads past
-// the last step are clamped to it (in bounds, written to stages of steps
-// past the last, which are not read again).
+// keep the compiler from regrouping it): 8 groups of 2 MFMAs (tiles (i, 0)
+// and (i, 1)), groups 0-3 on the sub-step-0 fragments f0 (i = group),
+// groups 4-7 on sub-step 1.  Fragment reads: sub-step 1 of this step into f1
+// during groups 0-2 (B fragments first), sub-step 0 of the next step into f0
+// during groups 4-6 (f0 is free after group 3).  Groups 0-3 also issue one
+// load each (step kt+4 into rl) and one LDS write each (step kt+2 from rw,
+// loaded during step kt-2), so the writes have long landed when the step
+// ends.  Then the barrier.  Branch-free: loads past the last step are
+// clamped to it (in bounds, written to stages of steps past the last, which
+// are not read again).
 template <bool F16>
-__device__ __forceinline__ void step(Smem& sm, v16i (&acc)[4][4], Frag& f0, Frag& f1,
-                                     Stage8& rl, const Stage8& rw, const Src& src, int kt,
+__device__ __forceinline__ void step(Smem& sm, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
+                                     Stage4& rl, const Stage4& rw, const Src& src, int kt,
                                      int last, int wm0, int wn0, const LoadMap& mp, int lane) {
   const int cur = kt % NBUF, nxt = (kt + 1) % NBUF, wst = (kt + 2) % NBUF;
   const char* ga;
@@ -208,6 +189,7 @@ __device__ __forceinline__ void step(Smem& sm, v16i (&acc)[4][4], Frag& f0, Frag
   const int r = lane & 31;
   const int ch1 = 2 + (lane >> 5);  // sub-step 1 chunk
   const int ch0 = (lane >> 5);      // sub-step 0 chunk
+  // fragment reads per group (6 per sub-step): b0 b1 | a0 a1 | a2 a3 | -
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
     const int i = g & 3;
@@ -215,29 +197,23 @@ __device__ __forceinline__ void step(Smem& sm, v16i (&acc)[4][4], Frag& f0, Frag
     Frag& fr = g < 4 ? f1 : f0;  // fragments read in this group
     const int rbuf = g < 4 ? cur : nxt;
     const int rch = g < 4 ? ch1 : ch0;
-    // fragment order over the four groups: b0 b1 | b2 b3 | a0 a1 | a2 a3
-    const int p0 = (g & 3) * 2;
-    v4i* dst0 = p0 < 4 ? &fr.b[p0] : &fr.a[p0 - 4];
-    v4i* dst1 = p0 < 4 ? &fr.b[p0 + 1] : &fr.a[p0 - 3];
-    const int row0 = p0 < 4 ? wn0 + p0 * 32 + r : wm0 + (p0 - 4) * 32 + r;
-    const int row1 = row0 + 32;
+    const int gg = g & 3;
     mma1<F16>(acc[i][0], fm.b[0], fm.a[i]);
     __builtin_amdgcn_sched_barrier(0);
-    *dst0 = p0 < 4 ? sm.b[rbuf][swz(row0, rch)] : sm.a[rbuf][swz(row0, rch)];
+    if (gg == 0) {
+      fr.b[0] = sm.b[rbuf][swz(wn0 + r, rch)];
+      fr.b[1] = sm.b[rbuf][swz(wn0 + 32 + r, rch)];
+    } else if (gg < 3) {
+      const int i0 = (gg - 1) * 2;
+      fr.a[i0] = sm.a[rbuf][swz(wm0 + i0 * 32 + r, rch)];
+      fr.a[i0 + 1] = sm.a[rbuf][swz(wm0 + (i0 + 1) * 32 + r, rch)];
+    }
     __builtin_amdgcn_sched_barrier(0);
     mma1<F16>(acc[i][1], fm.b[1], fm.a[i]);
     __builtin_amdgcn_sched_barrier(0);
-    *dst1 = p0 < 4 ? sm.b[rbuf][swz(row1, rch)] : sm.a[rbuf][swz(row1, rch)];
-    __builtin_amdgcn_sched_barrier(0);
-    mma1<F16>(acc[i][2], fm.b[2], fm.a[i]);
-    __builtin_amdgcn_sched_barrier(0);
-    gload1(rl, ga, gb, g, mp);
-    __builtin_amdgcn_sched_barrier(0);
-    mma1<F16>(acc[i][3], fm.b[3], fm.a[i]);
-    __builtin_amdgcn_sched_barrier(0);
     if (g < 4) {
-      lwrite1(sm, wst, rw, 2 * g, mp);
-      lwrite1(sm, wst, rw, 2 * g + 1, mp);
+      gload1(rl, ga, gb, g, mp);
+      lwrite1(sm, wst, rw, g, mp);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -252,8 +228,8 @@ __device__ __forceinline__ void step(Smem& sm, v16i (&acc)[4][4], Frag& f0, Frag
 // (step kt loads step kt+4 into buf[(kt+1)%3] and writes step kt+2 from
 // buf[(kt+2)%3]).  Unrolled by three so that the roles are static.
 template <bool F16>
-__device__ __forceinline__ void run_steps(Smem& sm, v16i (&acc)[4][4], Frag& f0, Frag& f1,
-                                          Stage8& b0, Stage8& b1, Stage8& b2, const Src& src,
+__device__ __forceinline__ void run_steps(Smem& sm, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
+                                          Stage4& b0, Stage4& b1, Stage4& b2, const Src& src,
                                           int k0, int k1, int last, int wm0, int wn0,
                                           const LoadMap& mp, int lane) {
   int kt = k0;
@@ -280,7 +256,7 @@ __device__ __forceinline__ void run_steps(Smem& sm, v16i (&acc)[4][4], Frag& f0,
 // Pipeline prologue: steps 0 and 1 into stages 0 and 1 (through buffers 0
 // and 1), then the loads of steps 2 and 3 into buffers 2 and 0, the first
 // fragments of step 0.
-__device__ __forceinline__ void prologue(Smem& sm, Frag& f0, Stage8& b0, Stage8& b1, Stage8& b2,
+__device__ __forceinline__ void prologue(Smem& sm, Frag& f0, Stage4& b0, Stage4& b1, Stage4& b2,
                                          const Src& src, int last, int wm0, int wn0,
                                          const LoadMap& mp, int lane) {
   gload_all(b0, src, 0, mp);
@@ -294,46 +270,45 @@ __device__ __forceinline__ void prologue(Smem& sm, Frag& f0, Stage8& b0, Stage8&
   fload(f0, sm, 0, 0, wm0, wn0, lane);
 }
 
-// The MFMAs take the W fragment as their first operand, so accumulator
-// element r of lane `lane` for tile (i, j) holds C at row i*32 + lane%32 and
-// column j*32 + acc_col(r, lane) of the wave block: a lane owns one row and
-// runs of 4 consecutive columns.
+// Accumulator element r of lane `lane` for tile (i, j) holds C at row
+// i*32 + lane%32 and column j*32 + acc_col(r, lane) of the wave block: a
+// lane owns one row and runs of 4 consecutive columns.
 __device__ __forceinline__ int acc_col(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
-// Stores one 32x128 row group of the wave block (fp32, accumulator layout)
-// as fp16 Y rows m_base .. m_base+31, columns n_col0 + 8*(lane%16) .. +7 per
-// lane on the way out, through the wave's 8 KiB staging area ys: each lane
-// writes its 4-column runs as 8-byte pieces (piece k of row r at position
-// k ^ 2*(r%16): the 32 rows of one write instruction spread over the banks),
-// then reads whole 16-byte row pieces back for 256-byte row-segment stores.
-__device__ __forceinline__ void store_rows(const v16f (&y)[4], uint16_t* ys,
+// Stores one 32x64 row group of the wave block (fp32, accumulator layout)
+// as fp16 Y rows m_base .. m_base+31, columns n_base .. n_base+63, through
+// the wave's 4 KiB staging area ys: each lane writes its 4-column runs as
+// 8-byte pieces (piece k of row r at position k ^ 2*((r/2)%8), which spreads
+// the 32 rows of a write over the banks), then reads whole 16-byte pieces
+// back for 128-byte row-segment stores.
+__device__ __forceinline__ void store_rows(const v16f (&y)[TJ], uint16_t* ys,
                                            uint16_t* __restrict__ Y, int M, int N, int m_base,
-                                           int n_col0, bool vec_store, int lane) {
+                                           int n_base, bool vec_store, int lane) {
   const int row = lane & 31;
-  const int sw = 2 * (row & 15);
+  const int sw = 2 * ((row >> 1) & 7);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < TJ; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int k = j * 8 + q * 2 + (lane >> 5);
       uint2 v;
       v.x = (uint32_t)f2h(y[j][4 * q]) | ((uint32_t)f2h(y[j][4 * q + 1]) << 16);
       v.y = (uint32_t)f2h(y[j][4 * q + 2]) | ((uint32_t)f2h(y[j][4 * q + 3]) << 16);
-      *reinterpret_cast<uint2*>(ys + row * 128 + (k ^ sw) * 4) = v;
+      *reinterpret_cast<uint2*>(ys + row * WN + (k ^ sw) * 4) = v;
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int c16 = lane & 15;
-  const int n_col = n_col0 + c16 * 8;
+  const int c16 = lane & 7;
+  const int n_col = n_base + c16 * 8;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int rl = p * 4 + (lane >> 4);  // row within the 32-row group
+  for (int p = 0; p < 4; ++p) {
+    const int rl = p * 8 + (lane >> 3);  // row within the 32-row group
     const int m = m_base + rl;
-    const int pos = (2 * c16) ^ (2 * (rl & 15));  // even: the pair stays in order
-    const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 128 + pos * 4);
+    const int pos = (2 * c16) ^ (2 * ((rl >> 1) & 7));  // even: the pair stays in order
+    const v4i v = *reinterpret_cast<const v4i*>(ys + rl * WN + pos * 4);
     if (m < M) {
       if (vec_store && n_col + 8 <= N) {
         // Y is written once and not read again here: stream it past the caches
@@ -351,6 +326,22 @@ __device__ __forceinline__ void store_rows(const v16f (&y)[4], uint16_t* ys,
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Tile of workgroup b, in an XCD-aware order: consecutive workgroups go
+// round-robin to the 8 XCDs, so each XCD gets a contiguous run of tiles, and
+// the tiles are walked in groups of 4 tile-rows so a run shares A and B
+// panels in its L2.
+__device__ __forceinline__ void tile_of(int b, int M, int N, int& tm, int& tn) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int G = tiles_m * tiles_n;
+  const int L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  constexpr int GROUP = 4;
+  const int per_group = GROUP * tiles_n;
+  const int first_m = (L / per_group) * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  tm = first_m + (L % per_group) % gsz;
+  tn = (L % per_group) / gsz;
+}
+
 }  // namespace
 
 // Many outlier columns (more than three fp16 steps): dequantize the int32
@@ -361,30 +352,18 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
     Smem& sm, const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int ldk,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale,
     const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-    const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
+    const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
-
-  // XCD-aware tile order: consecutive workgroups go round-robin to the 8
-  // XCDs, so give each XCD a contiguous run of tiles, and walk the tiles in
-  // groups of 4 tile-rows so the run shares A and B panels in its L2.
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int G = tiles_m * tiles_n;
-  const int b = blockIdx.x;
-  const int L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-  constexpr int GROUP = 4;
-  const int per_group = GROUP * tiles_n;
-  const int first_m = (L / per_group) * GROUP;
-  const int gsz = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (L % per_group) % gsz;
-  const int tn = (L % per_group) / gsz;
+  const int wm0 = (wave >> 2) * WM, wn0 = (wave & 3) * WN;
+  int tm, tn;
+  tile_of(blockIdx.x, M, N, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  v16i acc[4][4];
+  v16i acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
 
   const int nk8 = ldk / kTileK;
   const int nk16 = (*n_out + 31) / 32;
@@ -397,38 +376,18 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
   src.nk8 = nk8;
 
   const LoadMap mp = load_map(__builtin_amdgcn_readfirstlane(wave), lane);
-  Stage8 b0, b1, b2;
+  Stage4 b0, b1, b2;
   Frag f0, f1;
   prologue(sm, f0, b0, b1, b2, src, last, wm0, wn0, mp, lane);
-
-  // ---- int8 x int8 -> int32 over all K (outlier columns of Xq are zero)
   run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nk8, last, wm0, wn0, mp, lane);
 
-  if (false) {
-    wait_all();
+  // dequantize in place, fp32(C) * a_x[m] * a_w[n] / 127^2 (scales read from
+  // memory: every LDS stage is still in use), then the fp16 steps on top
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm0 + i * 32 + (lane & 31);
-          const int n = n0 + wn0 + j * 32 + acc_col(r, lane);
-          if (m < M && n < N) C[(size_t)m * N + n] = acc[i][j][r];
-        }
-    return;
-  }
-
-  const bool vec_store = (N & 7) == 0;
-
-  // ---- many outlier columns: dequantize in place, fp32(C) * a_x[m] * a_w[n]
-  // / 127^2 (scales read from memory: every LDS stage is still in use), and
-  // continue the pipeline over the fp16 steps on top.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TI; ++i) {
     const float sx = x_scale[min(m0 + wm0 + i * 32 + (lane & 31), M - 1)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       v16f f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -440,22 +399,22 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
   }
   run_steps<true>(sm, acc, f0, f1, b0, b1, b2, src, nk8, last + 1, last, wm0, wn0, mp, lane);
 
-  // store fp16 Y through LDS, 8 KiB per wave
+  // store fp16 Y through LDS, 4 KiB per wave
+  const bool vec_store = (N & 7) == 0;
   wait_all();
   __syncthreads();
-  uint16_t* ys = reinterpret_cast<uint16_t*>(&sm.a[0][0]) + wave * (32 * 128);
+  uint16_t* ys = reinterpret_cast<uint16_t*>(&sm.a[0][0]) + wave * (32 * WN);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v16f y[4];
+  for (int i = 0; i < TI; ++i) {
+    v16f y[TJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) y[j] = __builtin_bit_cast(v16f, acc[i][j]);
+    for (int j = 0; j < TJ; ++j) y[j] = __builtin_bit_cast(v16f, acc[i][j]);
     store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
   }
 }
 
-
 template <int MODE>  // 0: Y (fused epilogue), 1: int32 C
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
 k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int ldk,
                const float* __restrict__ x_scale, const float* __restrict__ w_scale,
                const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
@@ -463,32 +422,20 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
                int32_t* __restrict__ C) {
   __shared__ Smem sm;
   if (MODE == 0 && (*n_out + 31) / 32 > 3) {
-    gemm_tile_many_outliers(sm, Xq, Wq, M, N, ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
+    gemm_tile_many_outliers(sm, Xq, Wq, M, N, ldk, x_scale, w_scale, XO, WO, n_out, Y);
     return;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
-
-  // XCD-aware tile order: consecutive workgroups go round-robin to the 8
-  // XCDs, so give each XCD a contiguous run of tiles, and walk the tiles in
-  // groups of 4 tile-rows so the run shares A and B panels in its L2.
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int G = tiles_m * tiles_n;
-  const int b = blockIdx.x;
-  const int L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-  constexpr int GROUP = 4;
-  const int per_group = GROUP * tiles_n;
-  const int first_m = (L / per_group) * GROUP;
-  const int gsz = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (L % per_group) % gsz;
-  const int tn = (L % per_group) / gsz;
+  const int wm0 = (wave >> 2) * WM, wn0 = (wave & 3) * WN;
+  int tm, tn;
+  tile_of(blockIdx.x, M, N, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  v16i acc[4][4];
+  v16i acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
 
   const int nk8 = ldk / kTileK;
   const int nk16 = MODE == 0 ? (*n_out + 31) / 32 : 0;
@@ -501,7 +448,7 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   src.nk8 = nk8;
 
   const LoadMap mp = load_map(__builtin_amdgcn_readfirstlane(wave), lane);
-  Stage8 b0, b1, b2;
+  Stage4 b0, b1, b2;
   Frag f0, f1;
   prologue(sm, f0, b0, b1, b2, src, last, wm0, wn0, mp, lane);
 
@@ -511,9 +458,9 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   if (MODE == 1) {
     wait_all();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm0 + i * 32 + (lane & 31);
@@ -523,72 +470,67 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     return;
   }
 
+  // Few outlier steps (at most 3): steps nk8 and nk8+1 were written to LDS
+  // stages (nk8 + s) % NBUF by the int8 loop, step nk8+2 is still in
+  // registers (buffer (nk8+2) % 3) and is written here.  Stages
+  // (nk8 + 3) % NBUF and (nk8 + 4) % NBUF held the last two int8 steps, whose
+  // reads ended at the last barriers: the tile's scales go to the second,
+  // fp16 Y is staged in the first (4 KiB per wave).  Per 32-row group i:
+  // Y = fp32(C)*s read straight from the int32 accumulators, the outlier
+  // product accumulated on top, converted to fp16 and stored as 128-byte row
+  // segments.
   const bool vec_store = (N & 7) == 0;
-
+  float* s_x = reinterpret_cast<float*>(&sm.a[(nk8 + NBUF - 1) % NBUF][0]);
+  float* s_w = s_x + BM;
+  if (threadIdx.x < BM) {
+    const int t = threadIdx.x;
+    s_x[t] = x_scale[min(m0 + t, M - 1)];
+    s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
+  }
+  wait_all();
   {
-    // Few outlier steps (at most 3): steps nk8 and nk8+1 were written to LDS
-    // stages (nk8 + s) % NBUF by the int8 loop, step nk8+2 is still in
-    // registers (buffer (nk8+2) % 3) and is written here.  Stages
-    // (nk8 + 3) % NBUF and (nk8 + 4) % NBUF held the last two int8 steps,
-    // whose reads ended at the last barriers: the tile's scales go to the
-    // second, fp16 Y is staged in the first (8 KiB per wave).  Per 32-row
-    // group i: Y = fp32(C)*s read straight from the int32 accumulators, the
-    // outlier product accumulated on top, converted to fp16 and stored as
-    // 256-byte row segments.
-    float* s_x = reinterpret_cast<float*>(&sm.a[(nk8 + NBUF - 1) % NBUF][0]);
-    float* s_w = s_x + BM;
-    {
-      const int t = threadIdx.x;
-      s_x[t] = x_scale[min(m0 + t, M - 1)];
-      s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
-    }
-    wait_all();
-    {
-      const int w3 = (nk8 + 2) % NBUF;
-      const int rb = (nk8 + 2) % 3;
-      if (rb == 0)
-        lwrite_all(sm, w3, b0, mp);
-      else if (rb == 1)
-        lwrite_all(sm, w3, b1, mp);
-      else
-        lwrite_all(sm, w3, b2, mp);
-    }
-    __syncthreads();
-    const int fs = (nk8 + 3) % NBUF;
-    uint16_t* ys = reinterpret_cast<uint16_t*>(wave < 2 ? &sm.a[fs][0] : &sm.b[fs][0]) +
-                   (wave & 1) * (32 * 128);
+    const int w3 = (nk8 + 2) % NBUF;
+    const int rb = (nk8 + 2) % 3;
+    if (rb == 0)
+      lwrite_all(sm, w3, b0, mp);
+    else if (rb == 1)
+      lwrite_all(sm, w3, b1, mp);
+    else
+      lwrite_all(sm, w3, b2, mp);
+  }
+  __syncthreads();
+  const int fs = (nk8 + 3) % NBUF;
+  uint16_t* ys = reinterpret_cast<uint16_t*>(wave < 4 ? &sm.a[fs][0] : &sm.b[fs][0]) +
+                 (wave & 3) * (32 * WN);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // row group i: scaled int8 part first (its accumulator registers are
-      // then free for the fp16 MFMAs), outlier products accumulated on top
-      const float sx = s_x[wm0 + i * 32 + (lane & 31)];
-      v16f y[4];
+  for (int i = 0; i < TI; ++i) {
+    // row group i: scaled int8 part first (its accumulator registers are
+    // then free for the fp16 MFMAs), outlier products accumulated on top
+    const float sx = s_x[wm0 + i * 32 + (lane & 31)];
+    v16f y[TJ];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[wn0 + j * 32 + q * 8 + (lane >> 5) * 4]);
+      for (int q = 0; q < 4; ++q) {
+        const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[wn0 + j * 32 + q * 8 + (lane >> 5) * 4]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]);
-        }
-      for (int st = 0; st < nk16; ++st) {
-        const int stg = (nk8 + st) % NBUF;
+        for (int e = 0; e < 4; ++e) y[j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]);
+      }
+    for (int st = 0; st < nk16; ++st) {
+      const int stg = (nk8 + st) % NBUF;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int ch = kk * 2 + (lane >> 5);
-          const v8h a = __builtin_bit_cast(v8h, sm.a[stg][swz(wm0 + i * 32 + (lane & 31), ch)]);
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ch = kk * 2 + (lane >> 5);
+        const v8h a = __builtin_bit_cast(v8h, sm.a[stg][swz(wm0 + i * 32 + (lane & 31), ch)]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v8h b = __builtin_bit_cast(v8h, sm.b[stg][swz(wn0 + j * 32 + (lane & 31), ch)]);
-            y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, y[j], 0, 0, 0);
-          }
+        for (int j = 0; j < TJ; ++j) {
+          const v8h b = __builtin_bit_cast(v8h, sm.b[stg][swz(wn0 + j * 32 + (lane & 31), ch)]);
+          y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, y[j], 0, 0, 0);
         }
       }
-      store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
     }
-    return;
+    store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
   }
-
 }
 
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int ldk,

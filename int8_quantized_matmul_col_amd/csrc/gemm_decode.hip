@@ -23,6 +23,8 @@ namespace i8mm {
 namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+constexpr int kU = 2;  // K steps per loop iteration
+constexpr int kSlots = 8;  // outlier K steps parked in LDS (more: static schedule)
 constexpr int kMaxWords = (133144 + 63) / 64 * 2;  // mask words for the largest K
 }  // namespace
 
@@ -34,26 +36,45 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
   __shared__ uint32_t s_bits[kMaxWords];
   __shared__ int s_red[kWaves][G * 256];
-  __shared__ int s_any;
+  __shared__ v4i s_wslot[kSlots][G][64];  // Wq fragments of the outlier steps
+  __shared__ int s_slot_step[kSlots];
+  __shared__ int s_nslots;
+  __shared__ int s_next;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nw = ldk / 32;
-  if (t == 0) s_any = 0;
-  __syncthreads();
-  {
-    uint32_t any = 0;
-    for (int w = t; w < nw; w += kThreads) {
-      const uint32_t b = mask_bits[w];
-      s_bits[w] = b;
-      any |= b;
-    }
-    if (any) s_any = 1;  // benign race: every writer stores 1
+  const int nsteps = ldk / 64;
+  if (t == 0) {
+    s_nslots = 0;
+    s_next = 0;
   }
   __syncthreads();
-  const bool has_outliers = s_any != 0;
+  for (int w = t; w < nw; w += kThreads) s_bits[w] = mask_bits[w];
+  __syncthreads();
+  // K steps holding outlier columns, in ascending order (one wave, ballots)
+  if (wave == 0) {
+    int cnt = 0;
+    for (int s0 = 0; s0 < nsteps; s0 += 64) {
+      const int st = s0 + lane;
+      const bool f = st < nsteps && (s_bits[2 * st] | s_bits[2 * st + 1]) != 0u;
+      const uint64_t bal = __ballot(f);
+      const int rank = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+      if (f && rank < kSlots) s_slot_step[rank] = st;
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) s_nslots = cnt;
+  }
+  __syncthreads();
+  const int n_oslots = s_nslots;
+  const bool has_outliers = n_oslots > 0;
+  // Few outlier steps: the int8 work is handed out dynamically (the waves of
+  // a workgroup finish together instead of the slowest setting the pace) and
+  // the outlier steps' Wq fragments are parked in LDS for a fixed-order fp16
+  // pass at the end (the result stays deterministic).  Many: static split
+  // with the outlier term inline.
+  const bool dynamic = n_oslots <= kSlots;
 
   const int n_base = blockIdx.x * (G * 16);
-  const int nsteps = ldk / 64;
   const int s0 = (nsteps * wave) / kWaves, s1 = (nsteps * (wave + 1)) / kWaves;
   const int ml = lane & 15;   // row of the Xq fragment / column of the result
   const int kq = (lane >> 4) * 16;  // byte offset of this lane inside the 64-byte step
@@ -75,43 +96,115 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     acco[g] = v4f{};
   }
 
-  for (int s = s0; s < s1; ++s) {
-    const size_t off = (size_t)s * kTileBytes;
-    v4i b[G];
+  // fp16 outlier term of step s for this lane's 16 columns k0 .. k0+15 (b:
+  // the step's Wq fragments, already in registers)
+  auto outlier_step = [&](int s, const v4i (&b)[G]) {
+    const int k0 = s * 64 + kq;
+    const uint32_t ob = (s_bits[k0 >> 5] >> (k0 & 31)) & 0xffffu;
+    v8h xa[2];
 #pragma unroll
-    for (int g = 0; g < G; ++g) b[g] = *reinterpret_cast<const v4i*>(wrow[g] + off);
-    v4i a = xvalid ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
+    for (int e = 0; e < 16; ++e) {
+      uint16_t v = 0;
+      if (((ob >> e) & 1u) && xvalid) v = X[(size_t)ml * K + k0 + e];
+      xa[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
+    }
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[g], acc[g], 0, 0, 0);
-
-    if (has_outliers && (s_bits[2 * s] | s_bits[2 * s + 1])) {
-      // fp16 outlier fragments for this lane's 16 columns k0 .. k0+15
-      const int k0 = s * 64 + kq;
-      const uint32_t ob = (s_bits[k0 >> 5] >> (k0 & 31)) & 0xffffu;
-      v8h xa[2];
+    for (int g = 0; g < G; ++g) {
+      const int n = min(n_base + g * 16 + ml, N - 1);
+      const float aw = w_scale[n];
+      v8h wb[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         uint16_t v = 0;
-        if (((ob >> e) & 1u) && xvalid) v = X[(size_t)ml * K + k0 + e];
-        xa[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int n = min(n_base + g * 16 + ml, N - 1);
-        const float aw = w_scale[n];
-        v8h wb[2];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          uint16_t v = 0;
-          if ((ob >> e) & 1u) {
-            const int q = (int)(int8_t)((b[g][e >> 2] >> ((e & 3) * 8)) & 0xff);
-            v = dequant_w_half(q, aw);
-          }
-          wb[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
+        if ((ob >> e) & 1u) {
+          const int q = (int)(int8_t)((b[g][e >> 2] >> ((e & 3) * 8)) & 0xff);
+          v = dequant_w_half(q, aw);
         }
-        acco[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], wb[0], acco[g], 0, 0, 0);
-        acco[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], wb[1], acco[g], 0, 0, 0);
+        wb[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
       }
+      acco[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], wb[0], acco[g], 0, 0, 0);
+      acco[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], wb[1], acco[g], 0, 0, 0);
+    }
+  };
+  auto step_has_outliers = [&](int s) { return (s_bits[2 * s] | s_bits[2 * s + 1]) != 0u; };
+
+  if (dynamic) {
+    // chunks of kU steps from a workgroup counter, fetched one chunk ahead
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&s_next, kU);
+    base = __builtin_amdgcn_readfirstlane(base);
+    while (base < nsteps) {
+      int nb = 0;
+      if (lane == 0) nb = atomicAdd(&s_next, kU);
+      v4i b[kU][G];
+      v4i a[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int sl = min(base + u, nsteps - 1);  // a short last chunk re-reads, not counted
+        const size_t off = (size_t)sl * kTileBytes;
+#pragma unroll
+        for (int g = 0; g < G; ++g) b[u][g] = *reinterpret_cast<const v4i*>(wrow[g] + off);
+        a[u] = (xvalid && base + u < nsteps) ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][g], acc[g], 0, 0, 0);
+      if (has_outliers) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int st = min(base + u, nsteps - 1);
+          if (base + u < nsteps && step_has_outliers(st)) {
+            int k = 0;
+            while (s_slot_step[k] != st) ++k;  // present: at most kSlots entries
+#pragma unroll
+            for (int g = 0; g < G; ++g) s_wslot[k][g][lane] = b[u][g];
+          }
+        }
+      }
+      base = __builtin_amdgcn_readfirstlane(nb);
+    }
+    __syncthreads();
+    // fp16 outlier term, slot k on wave k % kWaves, in slot order
+    for (int k = wave; k < n_oslots; k += kWaves) {
+      v4i b[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) b[g] = s_wslot[k][g][lane];
+      outlier_step(s_slot_step[k], b);
+    }
+  } else {
+    // kU steps per iteration: all their loads are issued before the first
+    // MFMA, so a wave keeps kU*G KiB of weight reads in flight
+    int s = s0;
+    for (; s + kU <= s1; s += kU) {
+      v4i b[kU][G];
+      v4i a[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const size_t off = (size_t)(s + u) * kTileBytes;
+#pragma unroll
+        for (int g = 0; g < G; ++g) b[u][g] = *reinterpret_cast<const v4i*>(wrow[g] + off);
+        a[u] = xvalid ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][g], acc[g], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (step_has_outliers((s + u))) outlier_step((s + u), b[u]);
+    }
+    for (; s < s1; ++s) {
+      const size_t off = (size_t)s * kTileBytes;
+      v4i b[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) b[g] = *reinterpret_cast<const v4i*>(wrow[g] + off);
+      const v4i a = xvalid ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[g], acc[g], 0, 0, 0);
+      if (step_has_outliers(s)) outlier_step(s, b);
     }
   }
 

@@ -128,7 +128,8 @@ __global__ __launch_bounds__(256) void k_colmask(const uint16_t* __restrict__ X,
 // ---------------------------------------------------------------- row pass
 
 // Exclusive prefix counts of the mask words into s_pre[], mask words into
-// s_bits[]; returns |O|.  Called by all 256 threads of the block.
+// s_bits[] (from mask_bits; or already there when mask_bits is null); returns
+// |O|.  Called by all 256 threads of the block.
 __device__ int load_mask_prefix(const uint32_t* __restrict__ mask_bits, int nw,
                                 uint32_t* s_bits, int* s_pre) {
   __shared__ int s_wsum[4];
@@ -137,8 +138,13 @@ __device__ int load_mask_prefix(const uint32_t* __restrict__ mask_bits, int nw,
   const int w0 = min(nw, t * per), w1 = min(nw, w0 + per);
   int local = 0;
   for (int w = w0; w < w1; ++w) {
-    uint32_t b = mask_bits[w];
-    s_bits[w] = b;
+    uint32_t b;
+    if (mask_bits != nullptr) {
+      b = mask_bits[w];
+      s_bits[w] = b;
+    } else {
+      b = s_bits[w];
+    }
     local += __popc(b);
   }
   int incl = local;
@@ -206,11 +212,10 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ row, in
 // Bytes (or binary16 halves) of a chunk that belong to regular columns: the
 // mask bits ob (bit i = column i is an outlier) expanded to keep-masks.
 __device__ __forceinline__ uint32_t keep_bytes(uint32_t ob4) {
-  uint32_t k = 0xffffffffu;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if ((ob4 >> i) & 1u) k &= ~(0xffu << (8 * i));
-  return k;
+  // bit i of ob4 (< 16) moved to bit 8i (the shifted copies do not overlap),
+  // then widened to the whole byte
+  const uint32_t lsb = (ob4 * 0x00204081u) & 0x01010101u;
+  return ~(lsb * 0xffu);
 }
 __device__ __forceinline__ uint32_t keep_halves(uint32_t ob2) {
   return ((ob2 & 1u) ? 0u : 0xffffu) | ((ob2 & 2u) ? 0u : 0xffff0000u);
@@ -329,18 +334,19 @@ __device__ __forceinline__ void load_row(uint4 (&h)[CPL > 0 ? CPL : 1], const ui
   }
 }
 
-// Keep-masks of the chunks of lane rl (all ones on regular columns, zero on
-// the binary16 halves of outlier columns): the same for every row, so they
-// are built once per block.
+// Mask bytes of the chunks of lane rl (byte u of obs[u / 4] = mask bits of
+// chunk rl + u*LPR): the same for every row, so they are gathered once per
+// block.
 template <int CPL, int LPR>
-__device__ __forceinline__ void chunk_keep_masks(uint4 (&keep)[CPL > 0 ? CPL : 1],
+__device__ __forceinline__ void chunk_mask_bytes(uint32_t (&obs)[(CPL + 3) / 4 > 0 ? (CPL + 3) / 4 : 1],
                                                  const uint32_t* s_bits, int rl, int nch) {
+#pragma unroll
+  for (int i = 0; i < (CPL + 3) / 4; ++i) obs[i] = 0u;
 #pragma unroll
   for (int u = 0; u < CPL; ++u) {
     const int c = rl + u * LPR;
     const uint32_t ob = c < nch ? (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u;
-    keep[u] = uint4{keep_halves(ob & 3u), keep_halves((ob >> 2) & 3u),
-                    keep_halves((ob >> 4) & 3u), keep_halves((ob >> 6) & 3u)};
+    obs[u >> 2] |= ob << ((u & 3) * 8);
   }
 }
 
@@ -351,12 +357,12 @@ struct OutlierRow {
   uint16_t v[4];
 };
 
-// One row m (< M) held in registers (CPL > 0): outlier columns zeroed by the
-// keep-masks, absmax of |x| (the regular columns), codes, stores.  With
+// One row m (< M) held in registers (CPL > 0): absmax of |x| over the
+// regular columns, codes (zero on the outlier columns), stores.  With
 // WPR == 4 the block's four waves share the row (block barriers inside).
 template <int WPR, int CPL>
 __device__ __forceinline__ void quant_row_regs(uint4 (&h)[CPL > 0 ? CPL : 1],
-                                               const uint4 (&keep)[CPL > 0 ? CPL : 1],
+                                               const uint32_t (&obs)[(CPL + 3) / 4 > 0 ? (CPL + 3) / 4 : 1],
                                                const uint16_t* __restrict__ X, int m, int K,
                                                int ldk, int rl, int nch, int total, int opad,
                                                const uint32_t* s_bits, const int* s_pre,
@@ -365,15 +371,22 @@ __device__ __forceinline__ void quant_row_regs(uint4 (&h)[CPL > 0 ? CPL : 1],
                                                float* __restrict__ x_scale,
                                                uint16_t* __restrict__ XO) {
   constexpr int LPR = 64 * WPR;
+  constexpr int NOB = (CPL + 3) / 4 > 0 ? (CPL + 3) / 4 : 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint16_t* row = X + (size_t)m * K;
+  // The mask bytes are the same for every row of the block; left visible,
+  // the masks derived from them get hoisted out of the row loop and held in
+  // some fifty registers.  An empty asm makes them opaque per row instead.
+  uint32_t ob_row[NOB];
+#pragma unroll
+  for (int i = 0; i < NOB; ++i) {
+    ob_row[i] = obs[i];
+    asm volatile("" : "+v"(ob_row[i]));
+  }
   uint32_t mx2 = 0;  // two packed 16-bit maxima of |x| bits
 #pragma unroll
-  for (int u = 0; u < CPL; ++u) {
-    h[u].x &= keep[u].x; h[u].y &= keep[u].y; h[u].z &= keep[u].z; h[u].w &= keep[u].w;
-    mx2 = pk_max_u16(mx2, pk_max_u16(pk_max_u16(h[u].x & 0x7fff7fffu, h[u].y & 0x7fff7fffu),
-                                     pk_max_u16(h[u].z & 0x7fff7fffu, h[u].w & 0x7fff7fffu)));
-  }
+  for (int u = 0; u < CPL; ++u)
+    mx2 = pk_max_u16(mx2, chunk_absmax2(h[u], (ob_row[u >> 2] >> ((u & 3) * 8)) & 0xffu));
   uint32_t mx = wave_max(max(mx2 & 0xffffu, mx2 >> 16));
   if (WPR > 1) {
     __syncthreads();  // s_red of the previous row has been read
@@ -383,22 +396,8 @@ __device__ __forceinline__ void quant_row_regs(uint4 (&h)[CPL > 0 ? CPL : 1],
   }
   const float a = h2f((uint16_t)mx);
   const float r = a == 0.0f ? 0.0f : 127.0f / a;
-  // codes: every chunk straight through (outlier columns hold +-0 -> code 0),
-  // then the chunks with a value near a half-integer again, exactly
-  uint2 q[CPL > 0 ? CPL : 1];
-  uint32_t slow = 0;
-#pragma unroll
-  for (int u = 0; u < CPL; ++u) {
-    float dev;
-    q[u] = quant8_fast(h[u], r, &dev);
-    slow |= dev > kTieGuard ? (1u << u) : 0u;
-  }
-  if (slow) {
-#pragma unroll
-    for (int u = 0; u < CPL; ++u)
-      if ((slow >> u) & 1u) q[u] = quant8_exact(h[u], a);
-  }
-  // outlier slice values (loads from the row just read: cache hits)
+  // outlier slice values first (loads from the row just read: cache hits),
+  // so that only stores are in flight once the codes start going out
   constexpr int kXoPer = 4;  // slice entries per lane and pass
   OutlierRow xo{{0, 0, 0, 0}};
   const bool xo_one_pass = opad <= kXoPer * LPR;
@@ -411,18 +410,24 @@ __device__ __forceinline__ void quant_row_regs(uint4 (&h)[CPL > 0 ? CPL : 1],
         xo.v[p] = row[k];
       }
     }
+    wait_vmem_all();
   }
-  // Loads and stores share the vector memory counter; with both in flight
-  // the compiler cannot count and waits for all of them at the next use of
-  // a load.  One explicit wait here, after the arithmetic, then the stores.
-  wait_vmem_all();
-  // chunk c = rl + u*LPR starts at byte 8c of the row: LPR*8/64 column
-  // blocks (of kTileBytes each) after chunk rl
+  // codes chunk by chunk, each stored at once: the fast quotient, the exact
+  // one for a chunk with a value near a half-integer, outlier columns zeroed.
+  // Chunk c = rl + u*LPR starts at byte 8c of the row: LPR*8/64 column
+  // blocks (of kTileBytes each) after chunk rl.
   int8_t* xq_lane = Xq + tiled_offset(m, (size_t)rl * 8, ldk);
   constexpr size_t kStep = (size_t)LPR * 8 / kTileK * kTileBytes;
 #pragma unroll
-  for (int u = 0; u < CPL; ++u)
-    if (rl + u * LPR < nch) *reinterpret_cast<uint2*>(xq_lane + u * kStep) = q[u];
+  for (int u = 0; u < CPL; ++u) {
+    float dev;
+    uint2 q = quant8_fast(h[u], r, &dev);
+    if (dev > kTieGuard) q = quant8_exact(h[u], a);
+    const uint32_t ob = (ob_row[u >> 2] >> ((u & 3) * 8)) & 0xffu;
+    q.x &= keep_bytes(ob & 0xfu);
+    q.y &= keep_bytes(ob >> 4);
+    if (rl + u * LPR < nch) *reinterpret_cast<uint2*>(xq_lane + u * kStep) = q;
+  }
   if (XO != nullptr) {
     if (xo_one_pass) {
 #pragma unroll
@@ -483,9 +488,9 @@ __device__ __forceinline__ void quant_row_stream(const uint16_t* __restrict__ X,
   if (rl == 0) x_scale[m] = a;
 }
 
-// Row pass.  grid = W_O blocks (16 weight rows each; only when WO !=
-// nullptr) followed by row blocks, so the small gather work overlaps the row
-// work instead of forming a tail.  WPR = waves per row: 1 (a wave per row, 4
+// Row pass.  grid = row blocks followed by W_O blocks (16 weight rows each;
+// only when WO != nullptr): the row blocks take the machine first, the small
+// gathers fill the slots their tail frees.  WPR = waves per row: 1 (a wave per row, 4
 // rows per block and pass, the blocks looping over the rows) or 4 (the whole
 // block on one row, for few rows).  CPL = 8-column chunks per lane held in
 // registers between the absmax and the quantize passes (0: re-read the row
@@ -508,12 +513,14 @@ __global__ __launch_bounds__(256) void k_quant_rows(
   uint32_t* s_bits = s_dyn;
   int* s_pre = reinterpret_cast<int*>(s_dyn + nw);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int rb = (int)blockIdx.x - n_wo_blocks;  // row block index (< 0: a W_O block)
+  // row blocks first, then the W_O blocks (they run in the row blocks' tail)
+  const int n_row_blocks = (int)gridDim.x - n_wo_blocks;
+  const int rb = (int)blockIdx.x < n_row_blocks ? (int)blockIdx.x : -1;  // -1: a W_O block
   constexpr int RPB = 4 / WPR;               // rows per block and pass
   constexpr int LPR = 64 * WPR;              // lanes per row
   const int rl = (wave % WPR) * 64 + lane;   // lane index within the row
   const int nch = ldk / 8;
-  const int mstride = ((int)gridDim.x - n_wo_blocks) * RPB;
+  const int mstride = n_row_blocks * RPB;
   int m = rb * RPB + wave / WPR;
   // the block's first row is loaded before the mask prefix, so the two
   // memory latencies overlap
@@ -555,7 +562,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(
     // ---- W_O[n][j] for 16 weight rows: one (row, j) item per thread and
     // pass, loads issued together.
     const bool in_lds = olist_in_lds;
-    const int n0 = blockIdx.x * kWoRows;
+    const int n0 = ((int)blockIdx.x - n_row_blocks) * kWoRows;
     const int nl = t >> 4, jl = t & 15;
     const int n = n0 + nl;
     if (n < N) {
@@ -586,11 +593,11 @@ __global__ __launch_bounds__(256) void k_quant_rows(
 
   // ---- rows m, m + mstride, ... (one pass for M <= 4 * kRowBlocks)
   if (CPL > 0) {
-    uint4 keep[CPL > 0 ? CPL : 1];
-    chunk_keep_masks<CPL, LPR>(keep, s_bits, rl, nch);
+    uint32_t obs[(CPL + 3) / 4 > 0 ? (CPL + 3) / 4 : 1];
+    chunk_mask_bytes<CPL, LPR>(obs, s_bits, rl, nch);
     for (bool first = true; m < M; m += mstride, first = false) {
       if (!first) load_row<CPL, LPR>(ha, X + (size_t)m * K, rl, nck);
-      quant_row_regs<WPR, CPL>(ha, keep, X, m, K, ldk, rl, nch, total, opad, s_bits, s_pre,
+      quant_row_regs<WPR, CPL>(ha, obs, X, m, K, ldk, rl, nch, total, opad, s_bits, s_pre,
                                s_olist, olist_in_lds, nw, s_red, Xq, x_scale, XO);
     }
   } else {
@@ -598,6 +605,114 @@ __global__ __launch_bounds__(256) void k_quant_rows(
       quant_row_stream<WPR>(X, m, K, ldk, vec, rl, nch, total, opad, s_bits, s_pre, s_red, Xq,
                             x_scale, XO);
   }
+}
+
+// ---------------------------------------------------------------- few rows
+
+// The whole activation pass for a few rows (decode shapes, M <= 16) in one
+// launch: grid = M workgroups; workgroup m reads all M rows (a few KiB each,
+// shared through L2) to form the column absmax and the mask itself, then
+// quantizes row m, which it kept in registers.  Workgroup 0 also writes the
+// mask words, |O| and the optional mask bytes and O list.  CPT = 8-column
+// chunks per thread (ldk <= 256 * 8 * CPT); rows are 16-byte aligned and
+// K % 8 == 0.  Dynamic LDS: 2*nw words.
+template <int CPT>
+__global__ __launch_bounds__(256) void k_activation_small(
+    const uint16_t* __restrict__ X, int M, int K, int ldk, float threshold,
+    uint8_t* __restrict__ mask8, uint32_t* __restrict__ mask_bits, int32_t* __restrict__ n_out,
+    int32_t* __restrict__ out_idx, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
+    uint16_t* __restrict__ XO) {
+  extern __shared__ uint32_t s_dyn[];
+  __shared__ uint32_t s_red[4];
+  const int nw = ldk / 32, nch = ldk / 8, nck = K >> 3;
+  uint32_t* s_bits = s_dyn;
+  int* s_pre = reinterpret_cast<int*>(s_dyn + nw);
+  uint8_t* s_ob = reinterpret_cast<uint8_t*>(s_bits);  // mask byte of chunk c (little endian)
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int m = blockIdx.x;
+  const uint4* own_row = reinterpret_cast<const uint4*>(X + (size_t)m * K);
+
+  // ---- column absmax over the M rows, mask bytes (strict > threshold)
+  uint4 hv[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = t + u * 256;
+    uint32_t mx[4] = {0u, 0u, 0u, 0u};  // |x| bits, two columns per word
+    hv[u] = uint4{0u, 0u, 0u, 0u};
+    if (c < nck) {
+      // rows past M repeat row M-1 (no effect on the max), so all 16 loads
+      // are unconditional and in flight together
+      uint4 rows[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        rows[r] = reinterpret_cast<const uint4*>(X + (size_t)min(r, M - 1) * K)[c];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        mx[0] = pk_max_u16(mx[0], rows[r].x & 0x7fff7fffu);
+        mx[1] = pk_max_u16(mx[1], rows[r].y & 0x7fff7fffu);
+        mx[2] = pk_max_u16(mx[2], rows[r].z & 0x7fff7fffu);
+        mx[3] = pk_max_u16(mx[3], rows[r].w & 0x7fff7fffu);
+      }
+      hv[u] = own_row[c];
+    }
+    if (c < nch) {
+      uint32_t ob = 0;  // padding columns (k >= K) are never outliers
+      if (c < nck) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t hb = (mx[i >> 1] >> ((i & 1) * 16)) & 0xffffu;
+          ob |= (h2f((uint16_t)hb) > threshold ? 1u : 0u) << i;
+        }
+      }
+      s_ob[c] = (uint8_t)ob;
+    }
+  }
+  __syncthreads();
+  const int total = load_mask_prefix(nullptr, nw, s_bits, s_pre);
+  const int opad = (total + 63) & ~63;
+
+  if (m == 0) {
+    for (int w = t; w < nw; w += 256) mask_bits[w] = s_bits[w];
+    if (mask8 != nullptr)
+      for (int k = t; k < K; k += 256) mask8[k] = (uint8_t)((s_bits[k >> 5] >> (k & 31)) & 1u);
+    if (t == 0 && n_out != nullptr) *n_out = total;
+    if (out_idx != nullptr) {
+      for (int w = t; w < nw; w += 256) {
+        uint32_t b = s_bits[w];
+        int slot = s_pre[w];
+        while (b) {
+          out_idx[slot++] = w * 32 + __ffs(b) - 1;
+          b &= b - 1;
+        }
+      }
+    }
+  }
+
+  // ---- row m: absmax over the regular columns, codes, outlier slice
+  uint32_t mx2 = 0;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = t + u * 256;
+    const uint32_t ob = c < nch ? (uint32_t)s_ob[c] : 0u;
+    mx2 = pk_max_u16(mx2, chunk_absmax2(hv[u], ob));
+  }
+  uint32_t mx = wave_max(max(mx2 & 0xffffu, mx2 >> 16));
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  mx = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+  const float a = h2f((uint16_t)mx);
+  const float r = a == 0.0f ? 0.0f : 127.0f / a;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = t + u * 256;
+    if (c < nch)
+      *reinterpret_cast<uint2*>(Xq + tiled_offset(m, (size_t)c * 8, ldk)) =
+          code_chunk(hv[u], m, s_bits[c >> 2], (c & 3) * 8, s_pre[c >> 2], r, a, ldk, XO);
+  }
+  if (XO != nullptr)
+    for (int j = total + t; j < opad; j += 256)
+      XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = 0;
+  if (t == 0) x_scale[m] = a;
 }
 
 __global__ void k_zero_half(uint16_t* __restrict__ Y, int64_t count) {
@@ -665,6 +780,27 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
     else QR(1, 0);
   }
 #undef QR
+  return hipGetLastError();
+}
+
+bool activation_small_ok(const uint16_t* X, int M, int K, int ldk) {
+  return M >= 1 && M <= 16 && (K % 8) == 0 && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
+         ldk / 8 <= 256 * 8;
+}
+
+hipError_t launch_activation_small(const uint16_t* X, int M, int K, int ldk, float threshold,
+                                   uint8_t* mask8, uint32_t* mask_bits, int32_t* n_out,
+                                   int32_t* out_idx, int8_t* Xq, float* x_scale, uint16_t* XO,
+                                   hipStream_t s) {
+  const int nch = ldk / 8;
+  const size_t lds = (size_t)2 * (ldk / 32) * sizeof(uint32_t);
+  const int cpt = (nch + 255) / 256;
+#define AS(C) hipLaunchKernelGGL((k_activation_small<C>), dim3(M), dim3(256), lds, s, X, M, K, ldk, threshold, mask8, mask_bits, n_out, out_idx, Xq, x_scale, XO)
+  if (cpt <= 1) AS(1);
+  else if (cpt <= 2) AS(2);
+  else if (cpt <= 4) AS(4);
+  else AS(8);
+#undef AS
   return hipGetLastError();
 }
 

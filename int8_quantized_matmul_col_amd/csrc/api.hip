@@ -117,18 +117,33 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
   uint16_t* xo = out.X_O ? out.X_O : (L.decode ? nullptr : at<uint16_t>(ws, L.xo));
   uint16_t* wo = out.W_O ? out.W_O : (L.decode ? nullptr : at<uint16_t>(ws, L.wo));
 
-  if (L.decode) {
-    if ((e = i8mm::launch_colmask(X, nullptr, 0, m, k, ldk, threshold, out.mask, bits, s)) != hipSuccess)
+  if (L.decode && i8mm::activation_small_ok(X, m, k, ldk)) {
+    // mask and row codes in one launch; the W_O gather (only when asked
+    // for) in a launch of its own
+    if ((e = i8mm::launch_activation_small(X, m, k, ldk, threshold, out.mask, bits, count,
+                                           out.outlier_idx, xq, xs, xo, s)) != hipSuccess)
+      return hip_fail(e);
+    if (wo != nullptr &&
+        (e = i8mm::launch_quant_rows(X, 0, k, ldk, bits, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, Wq, w_scale, n, wo, s)) != hipSuccess)
       return hip_fail(e);
   } else {
-    uint16_t* part = at<uint16_t>(ws, L.part);
-    if ((e = i8mm::launch_colmax_partial(X, m, k, ldk, part, s)) != hipSuccess) return hip_fail(e);
-    if ((e = i8mm::launch_colmask(X, part, L.rc, m, k, ldk, threshold, out.mask, bits, s)) != hipSuccess)
+    if (L.decode) {
+      if ((e = i8mm::launch_colmask(X, nullptr, 0, m, k, ldk, threshold, out.mask, bits, s)) !=
+          hipSuccess)
+        return hip_fail(e);
+    } else {
+      uint16_t* part = at<uint16_t>(ws, L.part);
+      if ((e = i8mm::launch_colmax_partial(X, m, k, ldk, part, s)) != hipSuccess)
+        return hip_fail(e);
+      if ((e = i8mm::launch_colmask(X, part, L.rc, m, k, ldk, threshold, out.mask, bits, s)) !=
+          hipSuccess)
+        return hip_fail(e);
+    }
+    if ((e = i8mm::launch_quant_rows(X, m, k, ldk, bits, xq, xs, xo, count, out.outlier_idx, Wq,
+                                     w_scale, n, wo, s)) != hipSuccess)
       return hip_fail(e);
   }
-  if ((e = i8mm::launch_quant_rows(X, m, k, ldk, bits, xq, xs, xo, count, out.outlier_idx, Wq,
-                                   w_scale, n, wo, s)) != hipSuccess)
-    return hip_fail(e);
 
   uint16_t* Y = out.C ? nullptr : out.Y;
   if (out.C == nullptr && Y == nullptr) return INT8MM_OK;

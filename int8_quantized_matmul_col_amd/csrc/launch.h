@@ -44,5 +44,12 @@ hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, 
                               hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // Y[0 .. count) = 0 (K == 0 case).
 hipError_t launch_zero_half(uint16_t* Y, int64_t count, hipStream_t s);
+// Few rows (M <= 16): mask and row quantization in one launch (grid = M).
+// Applicable when activation_small_ok(); X_O optional, no W_O.
+bool activation_small_ok(const uint16_t* X, int M, int K, int ldk);
+hipError_t launch_activation_small(const uint16_t* X, int M, int K, int ldk, float threshold,
+                                   uint8_t* mask8, uint32_t* mask_bits, int32_t* n_out,
+                                   int32_t* out_idx, int8_t* Xq, float* x_scale, uint16_t* XO,
+                                   hipStream_t s);
 
 }  // namespace i8mm

@@ -282,7 +282,7 @@ __device__ __forceinline__ int acc_col(int r, int lane) {
 // the wave's 4 KiB staging area ys: each lane writes its 4-column runs as
 // 8-byte pieces (piece k of row r at position k ^ 2*((r/2)%8), which spreads
 // the 32 rows of a write over the banks), then reads whole 16-byte pieces
-// back for 128-byte row-segment stores.
+// back for 128-byte row-segment stores (whole cache lines).
 __device__ __forceinline__ void store_rows(const v16f (&y)[TJ], uint16_t* ys,
                                            uint16_t* __restrict__ Y, int M, int N, int m_base,
                                            int n_base, bool vec_store, int lane) {
@@ -311,8 +311,9 @@ __device__ __forceinline__ void store_rows(const v16f (&y)[TJ], uint16_t* ys,
     const v4i v = *reinterpret_cast<const v4i*>(ys + rl * WN + pos * 4);
     if (m < M) {
       if (vec_store && n_col + 8 <= N) {
-        // Y is written once and not read again here: stream it past the caches
-        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col));
+        // plain stores: the nontemporal form doubled the HBM write bytes
+        // (WRITE_SIZE) for the same Y
+        *reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col) = v;
       } else {
         const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
 #pragma unroll

@@ -29,8 +29,11 @@ constexpr int kRowChunk = kColmaxRowsPerChunk;
 
 // ---------------------------------------------------------------- column absmax
 
-// grid = ceil(ldk/512) column blocks x ceil(M/kRowChunk) row chunks (column block
-// fastest).  Block 256 = 64 column lanes x 4 row lanes; each lane reads 8
+// grid = ceil(ldk/512) column blocks x ceil(M/kRowChunk) row chunks.  Workgroups
+// go round-robin to the 8 XCDs; when the chunk count is a multiple of 8,
+// chunk c is read only by workgroups on XCD c % 8 (each XCD reads whole rows,
+// which its L2 then holds for the row pass); otherwise column block fastest.
+// Block 256 = 64 column lanes x 4 row lanes; each lane reads 8
 // consecutive columns (16 bytes) of kRowChunk/4 rows of the chunk, all loads issued
 // before use.  A wave reads one 1 KiB row segment per load instruction.
 __global__ __launch_bounds__(256) void k_colmax_partial(const uint16_t* __restrict__ X, int M,
@@ -38,7 +41,16 @@ __global__ __launch_bounds__(256) void k_colmax_partial(const uint16_t* __restri
                                                         uint16_t* __restrict__ part) {
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int ncb = (ldk + kColBlock - 1) / kColBlock;
-  const int cb = blockIdx.x % ncb, rcix = blockIdx.x / ncb;
+  const int rcn = (int)gridDim.x / ncb;
+  int cb, rcix;
+  if (rcn % 8 == 0) {
+    const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
+    rcix = 8 * (q / ncb) + x;
+    cb = q % ncb;
+  } else {
+    cb = blockIdx.x % ncb;
+    rcix = blockIdx.x / ncb;
+  }
   const int c0 = cb * kColBlock + tx * 8;
   const int r0 = rcix * kRowChunk;
   uint32_t mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -497,6 +509,17 @@ __device__ __forceinline__ void quant_row_stream(const uint16_t* __restrict__ X,
 // from L1/L2 instead, for long rows).
 // Dynamic LDS: 2*nw words plus the O list (up to kOListCap entries).
 constexpr int kOListCap = 4096;
+
+// Row group (of 4 rows) of row block rb in the one-wave-per-row form: with a
+// multiple of 128 row blocks, the groups of column-absmax chunk c (16 groups
+// of 64 rows) go to blocks on XCD c % 8, the XCD that read those rows in the
+// column-absmax pass, so that the rows are re-read from its L2.
+__device__ __forceinline__ int row_group_of(int rb, int n_row_blocks) {
+  static_assert(kRowChunk == 64, "16 row groups of 4 rows per column-absmax chunk");
+  if (n_row_blocks % 128 != 0) return rb;
+  const int x = rb & 7, q = rb >> 3;
+  return 16 * (8 * (q >> 4) + x) + (q & 15);
+}
 constexpr int kWoRows = 16;
 constexpr int kRowBlocks = 2048;  // row blocks of the one-wave-per-row form
 
@@ -521,7 +544,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(
   const int rl = (wave % WPR) * 64 + lane;   // lane index within the row
   const int nch = ldk / 8;
   const int mstride = n_row_blocks * RPB;
-  int m = rb * RPB + wave / WPR;
+  int m = (WPR == 1 && rb >= 0 ? row_group_of(rb, n_row_blocks) : rb) * RPB + wave / WPR;
   // the block's first row is loaded before the mask prefix, so the two
   // memory latencies overlap
   uint4 ha[CPL > 0 ? CPL : 1];

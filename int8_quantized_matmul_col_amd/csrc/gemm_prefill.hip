@@ -173,19 +173,23 @@ __device__ __forceinline__ void mma1(v16i& acc, const v4i& w, const v4i& x) {
 // groups 4-7 on sub-step 1.  Fragment reads: sub-step 1 of this step into f1
 // during groups 0-2 (B fragments first), sub-step 0 of the next step into f0
 // during groups 4-6 (f0 is free after group 3).  Groups 0-3 also issue one
-// load each (step kt+4 into rl) and one LDS write each (step kt+2 from rw,
-// loaded during step kt-2), so the writes have long landed when the step
-// ends.  Then the barrier.  Branch-free: loads past the last step are
-// clamped to it (in bounds, written to stages of steps past the last, which
-// are not read again).
+// load each (step kt+5 into rl) and one LDS write each (step kt+3 from rw,
+// loaded during step kt-2).  The barrier comes after every second step
+// (sync: odd kt, and the last step of a run): a stage written in step j is
+// first read in step j+2, and one of steps j, j+1 ends with a barrier; the
+// stage written in step j last held step j-2, read in steps j-3 and j-2, and
+// one of steps j-2, j-1 ended with a barrier.  Branch-free otherwise: loads
+// past the last step are clamped to it (in bounds, written to stages of
+// steps past the last, which are not read again).
 template <bool F16>
 __device__ __forceinline__ void step(Smem& sm, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
                                      Stage4& rl, const Stage4& rw, const Src& src, int kt,
-                                     int last, int wm0, int wn0, const LoadMap& mp, int lane) {
-  const int cur = kt % NBUF, nxt = (kt + 1) % NBUF, wst = (kt + 2) % NBUF;
+                                     int last, int wm0, int wn0, const LoadMap& mp, int lane,
+                                     bool sync) {
+  const int cur = kt % NBUF, nxt = (kt + 1) % NBUF, wst = (kt + 3) % NBUF;
   const char* ga;
   const char* gb;
-  step_src(src, min(kt + 4, last), ga, gb);
+  step_src(src, min(kt + 5, last), ga, gb);
   const int r = lane & 31;
   const int ch1 = 2 + (lane >> 5);  // sub-step 1 chunk
   const int ch0 = (lane >> 5);      // sub-step 0 chunk
@@ -219,13 +223,15 @@ __device__ __forceinline__ void step(Smem& sm, v16i (&acc)[TI][TJ], Frag& f0, Fr
   }
   // LDS operations complete in order: lgkmcnt(2) leaves only the last two
   // fragment reads (needed from group 2 of the next step on) in flight, so
-  // this wave's writes of stage kt+2 have landed before the barrier
-  __builtin_amdgcn_s_waitcnt(0xc27f);
-  __builtin_amdgcn_s_barrier();
+  // this wave's stage writes have landed before the barrier
+  if (sync) {
+    __builtin_amdgcn_s_waitcnt(0xc27f);
+    __builtin_amdgcn_s_barrier();
+  }
 }
 
 // Steps kt of [k0, k1) in order; the register buffers rotate with kt mod 3
-// (step kt loads step kt+4 into buf[(kt+1)%3] and writes step kt+2 from
+// (step kt loads step kt+5 into buf[(kt+1)%3] and writes step kt+3 from
 // buf[(kt+2)%3]).  Unrolled by three so that the roles are static.
 template <bool F16>
 __device__ __forceinline__ void run_steps(Smem& sm, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
@@ -233,38 +239,42 @@ __device__ __forceinline__ void run_steps(Smem& sm, v16i (&acc)[TI][TJ], Frag& f
                                           int k0, int k1, int last, int wm0, int wn0,
                                           const LoadMap& mp, int lane) {
   int kt = k0;
+#define SYNC(k) (((k) & 1) != 0 || (k) == k1 - 1)
   // bring kt to a multiple of 3
   while (kt < k1 && kt % 3 != 0) {
     if (kt % 3 == 1)
-      step<F16>(sm, acc, f0, f1, b2, b0, src, kt, last, wm0, wn0, mp, lane);
+      step<F16>(sm, acc, f0, f1, b2, b0, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
     else
-      step<F16>(sm, acc, f0, f1, b0, b1, src, kt, last, wm0, wn0, mp, lane);
+      step<F16>(sm, acc, f0, f1, b0, b1, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
     ++kt;
   }
   for (; kt + 3 <= k1; kt += 3) {
-    step<F16>(sm, acc, f0, f1, b1, b2, src, kt, last, wm0, wn0, mp, lane);
-    step<F16>(sm, acc, f0, f1, b2, b0, src, kt + 1, last, wm0, wn0, mp, lane);
-    step<F16>(sm, acc, f0, f1, b0, b1, src, kt + 2, last, wm0, wn0, mp, lane);
+    step<F16>(sm, acc, f0, f1, b1, b2, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
+    step<F16>(sm, acc, f0, f1, b2, b0, src, kt + 1, last, wm0, wn0, mp, lane, SYNC(kt + 1));
+    step<F16>(sm, acc, f0, f1, b0, b1, src, kt + 2, last, wm0, wn0, mp, lane, SYNC(kt + 2));
   }
   if (kt < k1) {
-    step<F16>(sm, acc, f0, f1, b1, b2, src, kt, last, wm0, wn0, mp, lane);
+    step<F16>(sm, acc, f0, f1, b1, b2, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
     ++kt;
   }
-  if (kt < k1) step<F16>(sm, acc, f0, f1, b2, b0, src, kt, last, wm0, wn0, mp, lane);
+  if (kt < k1) step<F16>(sm, acc, f0, f1, b2, b0, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
+#undef SYNC
 }
 
-// Pipeline prologue: steps 0 and 1 into stages 0 and 1 (through buffers 0
-// and 1), then the loads of steps 2 and 3 into buffers 2 and 0, the first
-// fragments of step 0.
+// Pipeline prologue: steps 0, 1 and 2 into stages 0, 1 and 2 (through
+// buffers 0, 1 and 2), then the loads of steps 3 and 4 into buffers 2 and 0,
+// the first fragments of step 0.
 __device__ __forceinline__ void prologue(Smem& sm, Frag& f0, Stage4& b0, Stage4& b1, Stage4& b2,
                                          const Src& src, int last, int wm0, int wn0,
                                          const LoadMap& mp, int lane) {
   gload_all(b0, src, 0, mp);
   gload_all(b1, src, min(1, last), mp);
+  gload_all(b2, src, min(2, last), mp);
   lwrite_all(sm, 0, b0, mp);
   lwrite_all(sm, 1, b1, mp);
-  gload_all(b2, src, min(2, last), mp);
-  gload_all(b0, src, min(3, last), mp);
+  lwrite_all(sm, 2, b2, mp);
+  gload_all(b2, src, min(3, last), mp);
+  gload_all(b0, src, min(4, last), mp);
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_s_barrier();
   fload(f0, sm, 0, 0, wm0, wn0, lane);
@@ -471,11 +481,11 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     return;
   }
 
-  // Few outlier steps (at most 3): steps nk8 and nk8+1 were written to LDS
-  // stages (nk8 + s) % NBUF by the int8 loop, step nk8+2 is still in
-  // registers (buffer (nk8+2) % 3) and is written here.  Stages
-  // (nk8 + 3) % NBUF and (nk8 + 4) % NBUF held the last two int8 steps, whose
-  // reads ended at the last barriers: the tile's scales go to the second,
+  // Few outlier steps (at most 3): steps nk8 .. nk8+2 were written to LDS
+  // stages (nk8 + s) % NBUF by the int8 loop.  Stages (nk8 + 3) % NBUF and
+  // (nk8 + 4) % NBUF held the last two int8 steps, whose reads ended at the
+  // last barrier (the last step of the loop ends with one): the tile's
+  // scales go to the second,
   // fp16 Y is staged in the first (4 KiB per wave).  Per 32-row group i:
   // Y = fp32(C)*s read straight from the int32 accumulators, the outlier
   // product accumulated on top, converted to fp16 and stored as 128-byte row
@@ -489,16 +499,6 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
   }
   wait_all();
-  {
-    const int w3 = (nk8 + 2) % NBUF;
-    const int rb = (nk8 + 2) % 3;
-    if (rb == 0)
-      lwrite_all(sm, w3, b0, mp);
-    else if (rb == 1)
-      lwrite_all(sm, w3, b1, mp);
-    else
-      lwrite_all(sm, w3, b2, mp);
-  }
   __syncthreads();
   const int fs = (nk8 + 3) % NBUF;
   uint16_t* ys = reinterpret_cast<uint16_t*>(wave < 4 ? &sm.a[fs][0] : &sm.b[fs][0]) +

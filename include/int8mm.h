@@ -39,7 +39,9 @@
  *     to 64), and byte b of row r sits at
  *         ((r/256)*(row_bytes/64) + b/64)*16384 + (r%256)*64 + b%64,
  *     i.e. 256-row x 64-byte blocks of 16 KiB, contiguous.  Padding columns
- *     of Wq and Xq hold zeros.
+ *     of Wq and Xq hold zeros.  These buffers are read and written with
+ *     16-byte accesses: each must be 16-byte aligned (INT8MM_EINVAL
+ *     otherwise).
  */
 #ifndef INT8MM_H
 #define INT8MM_H

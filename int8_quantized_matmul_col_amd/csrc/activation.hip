@@ -448,10 +448,21 @@ __device__ __forceinline__ void quant_row_regs(uint4 (&h)[CPL > 0 ? CPL : 1],
         if (j < opad) XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = xo.v[p];
       }
     } else {
-      for (int j = rl; j < opad; j += LPR) {
-        uint16_t v = 0;
-        if (j < total) v = row[olist_in_lds ? s_olist[j] : select_outlier(s_bits, s_pre, nw, j)];
-        XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = v;
+      // long slices: 8 entries per lane and pass, loads issued together
+      constexpr int kXoU = 8;
+      for (int j0 = rl; j0 < opad; j0 += kXoU * LPR) {
+        uint16_t v[kXoU];
+#pragma unroll
+        for (int u = 0; u < kXoU; ++u) {
+          const int j = j0 + u * LPR;
+          v[u] = 0;
+          if (j < total) v[u] = row[olist_in_lds ? s_olist[j] : select_outlier(s_bits, s_pre, nw, j)];
+        }
+#pragma unroll
+        for (int u = 0; u < kXoU; ++u) {
+          const int j = j0 + u * LPR;
+          if (j < opad) XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = v[u];
+        }
       }
     }
   }
@@ -507,8 +518,14 @@ __device__ __forceinline__ void quant_row_stream(const uint16_t* __restrict__ X,
 // block on one row, for few rows).  CPL = 8-column chunks per lane held in
 // registers between the absmax and the quantize passes (0: re-read the row
 // from L1/L2 instead, for long rows).
-// Dynamic LDS: 2*nw words plus the O list (up to kOListCap entries).
-constexpr int kOListCap = 4096;
+// Dynamic LDS: 2*nw words plus the O list, olist_cap(ldk) entries: every
+// column while the whole stays within 64 KiB (ldk up to ~14.5K, so that even
+// |O| = K is gathered through LDS); beyond that, larger |O| falls back to
+// select_outlier.
+__host__ __device__ inline int olist_cap(int ldk) {
+  const int room = 16384 - 2 * (ldk / 32);  // 32-bit words left of 64 KiB
+  return ldk < room ? ldk : room;
+}
 
 // Row group (of 4 rows) of row block rb in the one-wave-per-row form: with a
 // multiple of 128 row blocks, the groups of column-absmax chunk c (16 groups
@@ -554,7 +571,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(
   const int opad = (total + 63) & ~63;
   // the O list in LDS when it fits (W_O gather, X_O slice)
   int* s_olist = reinterpret_cast<int*>(s_dyn + 2 * nw);
-  const bool olist_in_lds = total <= kOListCap;
+  const bool olist_in_lds = total <= olist_cap(ldk);
   if ((WO != nullptr || XO != nullptr) && olist_in_lds) {
     for (int w = t; w < nw; w += 256) {
       uint32_t b = s_bits[w];
@@ -582,33 +599,37 @@ __global__ __launch_bounds__(256) void k_quant_rows(
   }
 
   if (rb < 0) {
-    // ---- W_O[n][j] for 16 weight rows: one (row, j) item per thread and
-    // pass, loads issued together.
+    // ---- W_O[n][j] for 16 weight rows: lane jl of row nl makes the 8
+    // consecutive entries j0 .. j0+7 (j0 = 8*jl + 128*pass), one 16-byte
+    // store; its 8 gathers of int8 codes are issued together.  (More runs per
+    // pass measured slower, also at |O| = K.)
     const bool in_lds = olist_in_lds;
     const int n0 = ((int)blockIdx.x - n_row_blocks) * kWoRows;
     const int nl = t >> 4, jl = t & 15;
     const int n = n0 + nl;
     if (n < N) {
       const float aw = w_scale[n];
-      for (int j0 = 0; j0 < opad; j0 += 64) {
-        int q[4];
-        bool live[4];
+      for (int j0 = 8 * jl; j0 < opad; j0 += 128) {
+        int q[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = j0 + u * 16 + jl;
-          live[u] = j < total;
-          q[u] = 0;
-          if (live[u]) {
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + e;
+          q[e] = 0;
+          if (j < total) {
             const int k = in_lds ? s_olist[j] : select_outlier(s_bits, s_pre, nw, j);
-            q[u] = (int)Wq[tiled_offset(n, (size_t)k, ldk)];
+            q[e] = (int)Wq[tiled_offset(n, (size_t)k, ldk)];
           }
         }
+        uint32_t h[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = j0 + u * 16 + jl;
-          WO[tiled_offset(n, (size_t)j * 2, (size_t)ldk * 2) / 2] =
-              live[u] ? dequant_w_half(q[u], aw) : (uint16_t)0;
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t lo = j0 + e < total ? dequant_w_half(q[e], aw) : 0u;
+          const uint32_t hi = j0 + e + 1 < total ? dequant_w_half(q[e + 1], aw) : 0u;
+          h[e / 2] = lo | (hi << 16);
         }
+        // 16 bytes at byte 2*j0 of the row: inside one 64-byte block
+        *reinterpret_cast<uint4*>(WO + tiled_offset(n, (size_t)j0 * 2, (size_t)ldk * 2) / 2) =
+            uint4{h[0], h[1], h[2], h[3]};
       }
     }
     return;
@@ -783,7 +804,7 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
   const int n_row_blocks = few_rows ? M : min((M + 3) / 4, kRowBlocks);
   const int n_wo_blocks = WO != nullptr ? (N + kWoRows - 1) / kWoRows : 0;
   const size_t lds = (size_t)2 * (ldk / 32) * sizeof(uint32_t) +
-                     (WO != nullptr || XO != nullptr ? (size_t)kOListCap * sizeof(int) : 0);
+                     (WO != nullptr || XO != nullptr ? (size_t)olist_cap(ldk) * sizeof(int) : 0);
   dim3 grid(n_row_blocks + n_wo_blocks);
   const int lanes = 64 * wpr;
   const int cpl_needed = (ldk / 8 + lanes - 1) / lanes;
@@ -799,6 +820,7 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
     if (cpl_needed <= 2) QR(1, 2);
     else if (cpl_needed <= 4) QR(1, 4);
     else if (cpl_needed <= 8) QR(1, 8);
+    else if (cpl_needed <= 12) QR(1, 12);
     else if (cpl_needed <= 16) QR(1, 16);
     else QR(1, 0);
   }

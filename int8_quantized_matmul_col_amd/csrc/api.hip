@@ -57,6 +57,8 @@ int check_shape(int64_t M, int64_t K, int64_t N) {
   return INT8MM_OK;
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -84,6 +86,9 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
   if (!stages && out.Y == nullptr) return INT8MM_EINVAL;
   if (K > 0 && (X == nullptr || Wq == nullptr)) return INT8MM_EINVAL;
   if (w_scale == nullptr) return INT8MM_EINVAL;
+  // panel-tiled buffers take 16-byte loads and stores
+  if (!aligned16(Wq) || !aligned16(out.Xq) || !aligned16(out.X_O) || !aligned16(out.W_O))
+    return INT8MM_EINVAL;
   const Layout L = make_layout(M, K, N);
   if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0 || ws_bytes < L.total)
     return INT8MM_EWORKSPACE;
@@ -151,7 +156,7 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
     e = i8mm::launch_gemm_decode(xq, Wq, m, n, k, ldk, xs, w_scale, X, bits, Y, out.C, s, ev_start,
                                  ev_stop);
   else
-    e = i8mm::launch_gemm_prefill(xq, Wq, m, n, ldk, xs, w_scale, xo, wo, count, Y, out.C, s,
+    e = i8mm::launch_gemm_prefill(xq, Wq, m, n, k, ldk, xs, w_scale, xo, wo, count, Y, out.C, s,
                                   ev_start, ev_stop);
   if (e != hipSuccess) return hip_fail(e);
   return INT8MM_OK;
@@ -173,6 +178,7 @@ INT8MM_API int int8_prepare_weight(const int8mm_half* W, int64_t N, int64_t K, i
   if (N < 0 || K < 0 || K > INT8MM_MAX_K || N > kMaxRows) return INT8MM_ESHAPE;
   if (N == 0) return INT8MM_OK;
   if (w_scale == nullptr || (K > 0 && (W == nullptr || Wq == nullptr))) return INT8MM_EINVAL;
+  if (!aligned16(Wq)) return INT8MM_EINVAL;
   hipError_t e = i8mm::launch_prepare_weight(W, (int)N, (int)K, (int)ld_of(K), Wq, w_scale, stream);
   if (e != hipSuccess) return hip_fail(e);
   return INT8MM_OK;

@@ -355,12 +355,16 @@ __device__ __forceinline__ void tile_of(int b, int M, int N, int& tm, int& tn) {
 
 }  // namespace
 
-// Many outlier columns (more than three fp16 steps): dequantize the int32
-// accumulators in place and continue the pipeline over the fp16 steps on
-// top.  Kept out of line so that its register pressure does not shape the
-// common path's allocation; it recomputes the whole tile.
+// Many outlier columns (more than three fp16 steps).  The int8 steps run
+// through the pipeline as in the common path; then the int32 accumulators
+// are dequantized into fp32 accumulators and the fp16 steps follow in a
+// simpler loop of its own: one step per LDS stage (two stages alternating),
+// three register buffers so that each step's loads are issued two steps
+// before it is written to LDS, one barrier per step.  Kept out of line so
+// that its registers do not shape the common path's allocation.
 __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
-    Smem& sm, const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int ldk,
+    Smem& sm, const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
+    int ldk,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale,
     const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
     const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y) {
@@ -378,7 +382,6 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
 
   const int nk8 = ldk / kTileK;
   const int nk16 = (*n_out + 31) / 32;
-  const int last = nk8 + nk16 - 1;
   Src src;
   src.A = (const char*)Xq + (size_t)tm * nk8 * kTileBytes;
   src.B = (const char*)Wq + (size_t)tn * nk8 * kTileBytes;
@@ -388,52 +391,84 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
 
   const LoadMap mp = load_map(__builtin_amdgcn_readfirstlane(wave), lane);
   Stage4 b0, b1, b2;
-  Frag f0, f1;
-  prologue(sm, f0, b0, b1, b2, src, last, wm0, wn0, mp, lane);
-  run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nk8, last, wm0, wn0, mp, lane);
+  if (*n_out < K) {
+    // int8 part: the pipeline clamped to the int8 steps (with |O| = K every
+    // code is 0 and C = 0: skipped)
+    Frag f0, f1;
+    const int last8 = nk8 - 1;
+    prologue(sm, f0, b0, b1, b2, src, last8, wm0, wn0, mp, lane);
+    run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nk8, last8, wm0, wn0, mp, lane);
+  }
 
-  // dequantize in place, fp32(C) * a_x[m] * a_w[n] / 127^2 (scales read from
-  // memory: every LDS stage is still in use), then the fp16 steps on top
+  // fp32 accumulators: fp32(C) * a_x[m] * a_w[n] / 127^2
+  v16f yf[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
     const float sx = x_scale[min(m0 + wm0 + i * 32 + (lane & 31), M - 1)];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      v16f f;
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float sw = w_scale[min(n0 + wn0 + j * 32 + acc_col(r, lane), N - 1)] * kInv127Sq;
-        f[r] = (float)acc[i][j][r] * (sx * sw);
+        yf[i][j][r] = (float)acc[i][j][r] * (sx * sw);
       }
-      acc[i][j] = __builtin_bit_cast(v16i, f);
-    }
   }
-  run_steps<true>(sm, acc, f0, f1, b0, b1, b2, src, nk8, last + 1, last, wm0, wn0, mp, lane);
+
+  // fp16 steps st = 0 .. nk16-1 (pipeline steps nk8 + st): step st is in
+  // register buffer st % 3 and LDS stage st % 2
+  wait_all();
+  __syncthreads();  // every wave is done with the int8 stages
+  gload_all(b0, src, nk8, mp);
+  if (nk16 > 1) gload_all(b1, src, nk8 + 1, mp);
+  if (nk16 > 2) gload_all(b2, src, nk8 + 2, mp);
+  lwrite_all(sm, 0, b0, mp);
+  __syncthreads();
+  auto f16_step = [&](int st, Stage4& ld, const Stage4& wr) {
+    if (st + 3 < nk16) gload_all(ld, src, nk8 + st + 3, mp);
+    const int buf = st & 1;
+    Frag f[2];  // both sub-steps' fragments read up front
+    fload(f[0], sm, buf, 0, wm0, wn0, lane);
+    fload(f[1], sm, buf, 1, wm0, wn0, lane);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          yf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, f[kk].b[j]),
+                                                            __builtin_bit_cast(v8h, f[kk].a[i]),
+                                                            yf[i][j], 0, 0, 0);
+    // stage (st+1) % 2 was last read in step st-1, before the last barrier
+    if (st + 1 < nk16) lwrite_all(sm, (st + 1) & 1, wr, mp);
+    __syncthreads();
+  };
+  int st = 0;
+  for (; st + 3 <= nk16; st += 3) {
+    f16_step(st, b0, b1);
+    f16_step(st + 1, b1, b2);
+    f16_step(st + 2, b2, b0);
+  }
+  if (st < nk16) f16_step(st, b0, b1);
+  if (st + 1 < nk16) f16_step(st + 1, b1, b2);
 
   // store fp16 Y through LDS, 4 KiB per wave
   const bool vec_store = (N & 7) == 0;
-  wait_all();
-  __syncthreads();
   uint16_t* ys = reinterpret_cast<uint16_t*>(&sm.a[0][0]) + wave * (32 * WN);
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    v16f y[TJ];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) y[j] = __builtin_bit_cast(v16f, acc[i][j]);
-    store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
-  }
+  for (int i = 0; i < TI; ++i) store_rows(yf[i], ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
 }
 
 template <int MODE>  // 0: Y (fused epilogue), 1: int32 C
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
-k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int ldk,
+k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
+               int ldk,
                const float* __restrict__ x_scale, const float* __restrict__ w_scale,
                const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
                const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y,
                int32_t* __restrict__ C) {
   __shared__ Smem sm;
   if (MODE == 0 && (*n_out + 31) / 32 > 3) {
-    gemm_tile_many_outliers(sm, Xq, Wq, M, N, ldk, x_scale, w_scale, XO, WO, n_out, Y);
+    gemm_tile_many_outliers(sm, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, Y);
     return;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -534,17 +569,17 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   }
 }
 
-hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int ldk,
+hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
                                hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (C != nullptr)
     hipExtLaunchKernelGGL(k_gemm_prefill<1>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
-                          ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
+                          K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
   else
     hipExtLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
-                          ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
+                          K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
   return hipGetLastError();
 }
 

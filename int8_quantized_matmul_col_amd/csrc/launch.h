@@ -31,7 +31,7 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
                              uint16_t* WO, hipStream_t s);
 // Prefill tile GEMM: int8 MFMA over K, then fp16 MFMA over the outlier slice,
 // fused dequant epilogue (Y), or int32 accumulators only (C).
-hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int ldk,
+hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
                                hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);

@@ -128,6 +128,8 @@ def test_matmul_rejects_bad_arguments(lib):
     assert _mm(lib, ws=FAKE_WS + 16) == binding.INT8MM_EWORKSPACE
     need = lib.int8_matmul_workspace_size(4, 8, 4)
     assert _mm(lib, nbytes=need - 1) == binding.INT8MM_EWORKSPACE
+    # the panel-tiled weight takes 16-byte accesses
+    assert _mm(lib, Wq=FAKE + 8) == binding.INT8MM_EINVAL
 
 
 def test_matmul_empty_is_a_noop(lib):
@@ -152,6 +154,11 @@ def test_stages_rejects_bad_arguments(lib):
     assert f(*args(X=None)) == binding.INT8MM_EINVAL
     assert f(*args(ws=None)) == binding.INT8MM_EWORKSPACE
     assert f(*args(M=0)) == binding.INT8MM_OK
+    # misaligned panel-tiled stage outputs (Xq, X_O, W_O: argument slots 10, 12, 13)
+    for slot in (10, 12, 13):
+        a = args()
+        a[slot] = FAKE + 4
+        assert f(*a) == binding.INT8MM_EINVAL
 
 
 def test_prepare_weight_rejects_bad_arguments(lib):
@@ -162,6 +169,7 @@ def test_prepare_weight_rejects_bad_arguments(lib):
     assert f(None, 4, 8, FAKE, FAKE, None) == binding.INT8MM_EINVAL
     assert f(FAKE, 4, 8, None, FAKE, None) == binding.INT8MM_EINVAL
     assert f(FAKE, 4, 8, FAKE, None, None) == binding.INT8MM_EINVAL
+    assert f(FAKE, 4, 8, FAKE + 2, FAKE, None) == binding.INT8MM_EINVAL  # misaligned Wq
     assert f(FAKE, 0, 8, FAKE, FAKE, None) == binding.INT8MM_OK  # empty weight
 
 

@@ -28,6 +28,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -137,12 +138,18 @@ def ingest_pmc(config: str, fetch_dir: str, write_dir: str) -> int:
     ran in the same process."""
     import workloads
     case = workloads.config_case(config)
+    # the Y-output instantiation timed by the bench (MODE 0), not the int32-C
+    # one that the |O| probe before the timed region runs
     kname = "k_gemm_decode" if case.M <= 16 else "k_gemm_prefill"
+    kpat = re.compile(r"k_gemm_decode<\d+, 0>" if case.M <= 16 else r"k_gemm_prefill<0>")
     fetch = _pmc_means(fetch_dir, "FETCH_SIZE")
     write = _pmc_means(write_dir, "WRITE_SIZE")
 
     def pick(d, tag):
-        keys = [k for k in d if tag in k]
+        if tag == COPY_KERNEL_TAG:
+            keys = [k for k in d if tag in k]
+        else:
+            keys = [k for k in d if kpat.search(k)]
         if not keys:
             raise SystemExit(f"no kernel matching {tag!r} in {sorted(d)}")
         return max(keys, key=lambda k: d[k]) if tag == COPY_KERNEL_TAG else keys[0]

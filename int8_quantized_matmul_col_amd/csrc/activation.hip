@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(
     const uint32_t* __restrict__ mask_bits, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
     uint16_t* __restrict__ XO, int32_t* __restrict__ n_out, int32_t* __restrict__ out_idx,
     const int8_t* __restrict__ Wq, const float* __restrict__ w_scale, int N,
-    uint16_t* __restrict__ WO) {
+    uint16_t* __restrict__ WO, int32_t* __restrict__ zero_ctr, int n_zero) {
   extern __shared__ uint32_t s_dyn[];
   __shared__ uint32_t s_red[4];
   const int nw = ldk / 32;
@@ -585,6 +585,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(
   __syncthreads();
 
   if (rb == 0) {
+    // counters the GEMM of this call starts from zero
+    for (int i = t; i < n_zero; i += 256) zero_ctr[i] = 0;
     if (t == 0 && n_out != nullptr) *n_out = total;
     if (out_idx != nullptr) {
       for (int w = t; w < nw; w += 256) {
@@ -788,15 +790,15 @@ template <int WPR, int CPL>
 static void launch_qr(dim3 grid, size_t lds, hipStream_t s, const uint16_t* X, int M, int K,
                       int ldk, int vec, int nwb, const uint32_t* mb, int8_t* Xq, float* xs,
                       uint16_t* XO, int32_t* n_out, int32_t* out_idx, const int8_t* Wq,
-                      const float* ws, int N, uint16_t* WO) {
+                      const float* ws, int N, uint16_t* WO, int32_t* zc, int nz) {
   hipLaunchKernelGGL((k_quant_rows<WPR, CPL>), grid, dim3(256), lds, s, X, M, K, ldk, vec, nwb, mb,
-                     Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO);
+                     Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO, zc, nz);
 }
 
 hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uint32_t* mask_bits,
                              int8_t* Xq, float* x_scale, uint16_t* XO, int32_t* n_out,
                              int32_t* out_idx, const int8_t* Wq, const float* w_scale, int N,
-                             uint16_t* WO, hipStream_t s) {
+                             uint16_t* WO, int32_t* zero_ctr, int n_zero, hipStream_t s) {
   const int vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
   const bool few_rows = M <= 256;  // whole block per row keeps the GPU busy
   const int wpr = few_rows ? 4 : 1;
@@ -808,7 +810,7 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
   dim3 grid(n_row_blocks + n_wo_blocks);
   const int lanes = 64 * wpr;
   const int cpl_needed = (ldk / 8 + lanes - 1) / lanes;
-#define QR(W, C) launch_qr<W, C>(grid, lds, s, X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out, out_idx, Wq, w_scale, N, WO)
+#define QR(W, C) launch_qr<W, C>(grid, lds, s, X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out, out_idx, Wq, w_scale, N, WO, zero_ctr, n_zero)
   // rows held in registers need 16-byte loads (aligned X, K % 8 == 0)
   if (!vec) {
     if (wpr == 4) QR(4, 0); else QR(1, 0);

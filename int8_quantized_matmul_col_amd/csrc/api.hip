@@ -31,6 +31,9 @@ struct Layout {
   bool decode = false;
   int rc = 0;  // row chunks of the column-absmax pass (prefill path)
   size_t part = 0, bits = 0, count = 0, xscale = 0, xq = 0, xo = 0, wo = 0, total = 0;
+  bool split = false;  // prefill GEMM with K split over two workgroups per tile
+  int tiles = 0;
+  size_t ctr = 0, cpart = 0;
 };
 
 Layout make_layout(int64_t M, int64_t K, int64_t N) {
@@ -47,6 +50,10 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
   L.xq = off;     off += align_up(Mp * L.ldk);
   L.xo = off;     off += L.decode ? 0 : align_up(Mp * L.ldk * 2);
   L.wo = off;     off += L.decode ? 0 : align_up(Np * L.ldk * 2);
+  L.tiles = (int)(Mp / 256 * (Np / 256));
+  L.split = !L.decode && i8mm::gemm_prefill_split((int)M, (int)N, (int)L.ldk);
+  L.ctr = off;    off += L.split ? align_up((size_t)L.tiles * 4) : 0;
+  L.cpart = off;  off += L.split ? (size_t)L.tiles * 2 * 256 * 256 * 4 : 0;
   L.total = off < kAlign ? kAlign : off;
   return L;
 }
@@ -121,6 +128,10 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
   int8_t* xq = out.Xq ? out.Xq : at<int8_t>(ws, L.xq);
   uint16_t* xo = out.X_O ? out.X_O : (L.decode ? nullptr : at<uint16_t>(ws, L.xo));
   uint16_t* wo = out.W_O ? out.W_O : (L.decode ? nullptr : at<uint16_t>(ws, L.wo));
+  // K split in the GEMM (Y output only): its per-tile counters are zeroed by
+  // the row pass of this call
+  const bool split = L.split && out.C == nullptr && out.Y != nullptr;
+  int32_t* ctr = split ? at<int32_t>(ws, L.ctr) : nullptr;
 
   if (L.decode && i8mm::activation_small_ok(X, m, k, ldk)) {
     // mask and row codes in one launch; the W_O gather (only when asked
@@ -130,7 +141,7 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
       return hip_fail(e);
     if (wo != nullptr &&
         (e = i8mm::launch_quant_rows(X, 0, k, ldk, bits, nullptr, nullptr, nullptr, nullptr,
-                                     nullptr, Wq, w_scale, n, wo, s)) != hipSuccess)
+                                     nullptr, Wq, w_scale, n, wo, nullptr, 0, s)) != hipSuccess)
       return hip_fail(e);
   } else {
     if (L.decode) {
@@ -146,7 +157,8 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
         return hip_fail(e);
     }
     if ((e = i8mm::launch_quant_rows(X, m, k, ldk, bits, xq, xs, xo, count, out.outlier_idx, Wq,
-                                     w_scale, n, wo, s)) != hipSuccess)
+                                     w_scale, n, wo, split ? ctr : nullptr, split ? L.tiles : 0,
+                                     s)) != hipSuccess)
       return hip_fail(e);
   }
 
@@ -156,8 +168,9 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
     e = i8mm::launch_gemm_decode(xq, Wq, m, n, k, ldk, xs, w_scale, X, bits, Y, out.C, s, ev_start,
                                  ev_stop);
   else
-    e = i8mm::launch_gemm_prefill(xq, Wq, m, n, k, ldk, xs, w_scale, xo, wo, count, Y, out.C, s,
-                                  ev_start, ev_stop);
+    e = i8mm::launch_gemm_prefill(xq, Wq, m, n, k, ldk, xs, w_scale, xo, wo, count, Y, out.C,
+                                  split ? at<int32_t>(ws, L.cpart) : nullptr,
+                                  split ? ctr : nullptr, s, ev_start, ev_stop);
   if (e != hipSuccess) return hip_fail(e);
   return INT8MM_OK;
 }

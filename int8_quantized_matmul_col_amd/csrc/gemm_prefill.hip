@@ -458,6 +458,12 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
   for (int i = 0; i < TI; ++i) store_rows(yf[i], ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
 }
 
+// split (MODE 0 only): the grid is two workgroups per tile, workgroup
+// half*tiles + tile taking int8 steps [0, nk8/2) (half 0) or [nk8/2, nk8)
+// (half 1) of that tile.  Each stores its int32 partial in cpart; the second
+// to finish (per-tile counter ctr, zeroed by the activation pass of the same
+// call) adds the other's partial, an exact integer sum, and runs the
+// epilogue.  Used when there are too few tiles to fill the GPU.
 template <int MODE>  // 0: Y (fused epilogue), 1: int32 C
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
 k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
@@ -465,16 +471,22 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
                const float* __restrict__ x_scale, const float* __restrict__ w_scale,
                const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
                const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y,
-               int32_t* __restrict__ C) {
+               int32_t* __restrict__ C, int split, int32_t* __restrict__ cpart,
+               int32_t* __restrict__ ctr) {
   __shared__ Smem sm;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int half = split ? (int)blockIdx.x / tiles : 0;
+  const int tb = split ? (int)blockIdx.x % tiles : (int)blockIdx.x;
   if (MODE == 0 && (*n_out + 31) / 32 > 3) {
-    gemm_tile_many_outliers(sm, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, Y);
+    // whole tile in one workgroup (half 0 of a split grid is workgroup tb)
+    if (half == 0)
+      gemm_tile_many_outliers(sm, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, Y);
     return;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm0 = (wave >> 2) * WM, wn0 = (wave & 3) * WN;
   int tm, tn;
-  tile_of(blockIdx.x, M, N, tm, tn);
+  tile_of(tb, M, N, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   v16i acc[TI][TJ];
@@ -485,21 +497,58 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 
   const int nk8 = ldk / kTileK;
   const int nk16 = MODE == 0 ? (*n_out + 31) / 32 : 0;
-  const int last = nk8 + nk16 - 1;
+  // this workgroup's int8 steps [k0, k0 + nr); pipeline step s < nr is int8
+  // step k0 + s, then come the outlier steps
+  const int k0 = half ? nk8 / 2 : 0;
+  const int nr = split ? (half ? nk8 - nk8 / 2 : nk8 / 2) : nk8;
+  const int last = nr + nk16 - 1;
   Src src;
-  src.A = (const char*)Xq + (size_t)tm * nk8 * kTileBytes;
-  src.B = (const char*)Wq + (size_t)tn * nk8 * kTileBytes;
+  src.A = (const char*)Xq + ((size_t)tm * nk8 + k0) * kTileBytes;
+  src.B = (const char*)Wq + ((size_t)tn * nk8 + k0) * kTileBytes;
   src.AO = (const char*)XO + (size_t)tm * (2 * nk8) * kTileBytes;  // fp16 rows: 2*ldk bytes
   src.BO = (const char*)WO + (size_t)tn * (2 * nk8) * kTileBytes;
-  src.nk8 = nk8;
+  src.nk8 = nr;
 
   const LoadMap mp = load_map(__builtin_amdgcn_readfirstlane(wave), lane);
   Stage4 b0, b1, b2;
   Frag f0, f1;
   prologue(sm, f0, b0, b1, b2, src, last, wm0, wn0, mp, lane);
 
-  // ---- int8 x int8 -> int32 over all K (outlier columns of Xq are zero)
-  run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nk8, last, wm0, wn0, mp, lane);
+  // ---- int8 x int8 -> int32 over this workgroup's K steps (outlier
+  // columns of Xq are zero)
+  run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nr, last, wm0, wn0, mp, lane);
+
+  if (MODE == 0 && split) {
+    // partial of this half, one register per pass: 512 consecutive ints
+    constexpr int kRegs = TI * TJ * 16;
+    int32_t* mine = cpart + ((size_t)tb * 2 + half) * kRegs * NT + threadIdx.x;
+    const int32_t* other = cpart + ((size_t)tb * 2 + (half ^ 1)) * kRegs * NT + threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[((i * TJ + j) * 16 + r) * NT] = acc[i][j][r];
+    // the flag lives in stage (nr+3) % NBUF, free since the loop's last
+    // barrier and overwritten by the epilogue only after its own barrier
+    int* s_first = reinterpret_cast<int*>(&sm.a[(nr + 3) % NBUF][0]);
+    wait_all();       // this thread's stores have landed
+    __syncthreads();  // ... and every other thread's
+    if (threadIdx.x == 0) {
+      __threadfence();  // the partial is visible device-wide before the count
+      const int first = atomicAdd(&ctr[tb], 1) == 0;
+      if (!first) __threadfence();  // and the other half's is seen after it
+      *s_first = first;
+    }
+    __syncthreads();
+    if (*s_first) return;  // the other half finishes the tile
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += other[((i * TJ + j) * 16 + r) * NT];
+  }
 
   if (MODE == 1) {
     wait_all();
@@ -516,9 +565,9 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     return;
   }
 
-  // Few outlier steps (at most 3): steps nk8 .. nk8+2 were written to LDS
-  // stages (nk8 + s) % NBUF by the int8 loop.  Stages (nk8 + 3) % NBUF and
-  // (nk8 + 4) % NBUF held the last two int8 steps, whose reads ended at the
+  // Few outlier steps (at most 3): pipeline steps nr .. nr+2 were written to
+  // LDS stages (nr + s) % NBUF by the int8 loop.  Stages (nr + 3) % NBUF and
+  // (nr + 4) % NBUF held the last two int8 steps, whose reads ended at the
   // last barrier (the last step of the loop ends with one): the tile's
   // scales go to the second,
   // fp16 Y is staged in the first (4 KiB per wave).  Per 32-row group i:
@@ -526,7 +575,7 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   // product accumulated on top, converted to fp16 and stored as 128-byte row
   // segments.
   const bool vec_store = (N & 7) == 0;
-  float* s_x = reinterpret_cast<float*>(&sm.a[(nk8 + NBUF - 1) % NBUF][0]);
+  float* s_x = reinterpret_cast<float*>(&sm.a[(nr + NBUF - 1) % NBUF][0]);
   float* s_w = s_x + BM;
   if (threadIdx.x < BM) {
     const int t = threadIdx.x;
@@ -535,7 +584,7 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   }
   wait_all();
   __syncthreads();
-  const int fs = (nk8 + 3) % NBUF;
+  const int fs = (nr + 3) % NBUF;
   uint16_t* ys = reinterpret_cast<uint16_t*>(wave < 4 ? &sm.a[fs][0] : &sm.b[fs][0]) +
                  (wave & 3) * (32 * WN);
 #pragma unroll
@@ -553,7 +602,7 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
         for (int e = 0; e < 4; ++e) y[j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]);
       }
     for (int st = 0; st < nk16; ++st) {
-      const int stg = (nk8 + st) % NBUF;
+      const int stg = (nr + st) % NBUF;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int ch = kk * 2 + (lane >> 5);
@@ -572,15 +621,23 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
-                               hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                               int32_t* cpart, int32_t* ctr, hipStream_t s, hipEvent_t e0,
+                               hipEvent_t e1) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int split = (C == nullptr && cpart != nullptr) ? 1 : 0;
   if (C != nullptr)
     hipExtLaunchKernelGGL(k_gemm_prefill<1>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
-                          K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
+                          K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C, 0, nullptr, nullptr);
   else
-    hipExtLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
-                          K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C);
+    hipExtLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles * (split + 1)), dim3(NT), 0, s, e0, e1, 0,
+                          Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C, split,
+                          cpart, ctr);
   return hipGetLastError();
+}
+
+bool gemm_prefill_split(int M, int N, int ldk) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  return tiles <= 128 && ldk / kTileK >= 32;
 }
 
 }  // namespace i8mm

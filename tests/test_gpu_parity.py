@@ -39,6 +39,8 @@ SHAPES = [
     (64, 130, 40, 2, 0.0),         # every non-zero column is an outlier
     (96, 320, 96, 4, math.inf),    # pure int8
     (40, 96, 520, 90, 0.5),        # |O| close to K
+    (300, 2112, 520, 7, 6.0),      # K split over two workgroups per tile, odd step count
+    (260, 2048, 300, 2, 0.0),      # split grid with every column an outlier
 ]
 
 

@@ -20,6 +20,21 @@ int hip_fail(hipError_t e) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kLayoutCUs = 256;  // MI355X compute units
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // M and N: int32 indexing in the kernels
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -31,8 +46,7 @@ struct Layout {
   bool decode = false;
   int rc = 0;  // row chunks of the column-absmax pass (prefill path)
   size_t part = 0, bits = 0, count = 0, xscale = 0, xq = 0, xo = 0, wo = 0, total = 0;
-  bool split = false;  // prefill GEMM with K split over two workgroups per tile
-  int tiles = 0;
+  int nsplit = 0;  // prefill GEMM tiles computed by two workgroups (K split)
   size_t ctr = 0, cpart = 0;
 };
 
@@ -50,10 +64,11 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
   L.xq = off;     off += align_up(Mp * L.ldk);
   L.xo = off;     off += L.decode ? 0 : align_up(Mp * L.ldk * 2);
   L.wo = off;     off += L.decode ? 0 : align_up(Np * L.ldk * 2);
-  L.tiles = (int)(Mp / 256 * (Np / 256));
-  L.split = !L.decode && i8mm::gemm_prefill_split((int)M, (int)N, (int)L.ldk);
-  L.ctr = off;    off += L.split ? align_up((size_t)L.tiles * 4) : 0;
-  L.cpart = off;  off += L.split ? (size_t)L.tiles * 2 * 256 * 256 * 4 : 0;
+  // sized for a 256-CU MI355X; a call on a GPU of another CU count splits
+  // only when that fits (run())
+  L.nsplit = L.decode ? 0 : i8mm::gemm_prefill_nsplit((int)M, (int)N, (int)L.ldk, kLayoutCUs);
+  L.ctr = off;    off += align_up((size_t)L.nsplit * 4);
+  L.cpart = off;  off += (size_t)L.nsplit * 2 * 256 * 256 * 4;
   L.total = off < kAlign ? kAlign : off;
   return L;
 }
@@ -128,10 +143,14 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
   int8_t* xq = out.Xq ? out.Xq : at<int8_t>(ws, L.xq);
   uint16_t* xo = out.X_O ? out.X_O : (L.decode ? nullptr : at<uint16_t>(ws, L.xo));
   uint16_t* wo = out.W_O ? out.W_O : (L.decode ? nullptr : at<uint16_t>(ws, L.wo));
-  // K split in the GEMM (Y output only): its per-tile counters are zeroed by
-  // the row pass of this call
-  const bool split = L.split && out.C == nullptr && out.Y != nullptr;
-  int32_t* ctr = split ? at<int32_t>(ws, L.ctr) : nullptr;
+  // K split in the GEMM (Y output only, within the workspace's capacity):
+  // its counters are zeroed by the row pass of this call
+  int nsplit = 0;
+  if (!L.decode && out.C == nullptr && out.Y != nullptr && L.nsplit > 0) {
+    nsplit = i8mm::gemm_prefill_nsplit(m, n, ldk, device_cus());
+    if (nsplit > L.nsplit) nsplit = 0;
+  }
+  int32_t* ctr = nsplit ? at<int32_t>(ws, L.ctr) : nullptr;
 
   if (L.decode && i8mm::activation_small_ok(X, m, k, ldk)) {
     // mask and row codes in one launch; the W_O gather (only when asked
@@ -157,7 +176,7 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
         return hip_fail(e);
     }
     if ((e = i8mm::launch_quant_rows(X, m, k, ldk, bits, xq, xs, xo, count, out.outlier_idx, Wq,
-                                     w_scale, n, wo, split ? ctr : nullptr, split ? L.tiles : 0,
+                                     w_scale, n, wo, ctr, nsplit,
                                      s)) != hipSuccess)
       return hip_fail(e);
   }
@@ -169,8 +188,8 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
                                  ev_stop);
   else
     e = i8mm::launch_gemm_prefill(xq, Wq, m, n, k, ldk, xs, w_scale, xo, wo, count, Y, out.C,
-                                  split ? at<int32_t>(ws, L.cpart) : nullptr,
-                                  split ? ctr : nullptr, s, ev_start, ev_stop);
+                                  nsplit, nsplit ? at<int32_t>(ws, L.cpart) : nullptr, ctr, s,
+                                  ev_start, ev_stop);
   if (e != hipSuccess) return hip_fail(e);
   return INT8MM_OK;
 }

@@ -458,12 +458,14 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
   for (int i = 0; i < TI; ++i) store_rows(yf[i], ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
 }
 
-// split (MODE 0 only): the grid is two workgroups per tile, workgroup
-// half*tiles + tile taking int8 steps [0, nk8/2) (half 0) or [nk8/2, nk8)
-// (half 1) of that tile.  Each stores its int32 partial in cpart; the second
-// to finish (per-tile counter ctr, zeroed by the activation pass of the same
-// call) adds the other's partial, an exact integer sum, and runs the
-// epilogue.  Used when there are too few tiles to fill the GPU.
+// nsplit (MODE 0 only): the last nsplit tiles (in workgroup order) are each
+// computed by two workgroups, unit u = 0 .. nsplit-1 as workgroups
+// nwhole + u (half 0: int8 steps [0, nk8/2)) and nwhole + nsplit + u (half 1:
+// [nk8/2, nk8)), after the nwhole = tiles - nsplit whole tiles.  Each half
+// stores its int32 partial in cpart; the second to finish (counter ctr[u],
+// zeroed by the activation pass of the same call) adds the other's partial,
+// an exact integer sum, and runs the epilogue.  Used when the tiles would
+// leave most of the GPU idle.
 template <int MODE>  // 0: Y (fused epilogue), 1: int32 C
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
 k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
@@ -471,14 +473,21 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
                const float* __restrict__ x_scale, const float* __restrict__ w_scale,
                const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
                const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y,
-               int32_t* __restrict__ C, int split, int32_t* __restrict__ cpart,
+               int32_t* __restrict__ C, int nsplit, int32_t* __restrict__ cpart,
                int32_t* __restrict__ ctr) {
   __shared__ Smem sm;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int half = split ? (int)blockIdx.x / tiles : 0;
-  const int tb = split ? (int)blockIdx.x % tiles : (int)blockIdx.x;
+  const int nwhole = tiles - nsplit;
+  int tb = (int)blockIdx.x, half = 0, su = -1;  // su: split unit of this workgroup
+  if ((int)blockIdx.x >= nwhole) {
+    const int bb = (int)blockIdx.x - nwhole;
+    su = bb % nsplit;
+    half = bb / nsplit;
+    tb = nwhole + su;
+  }
+  const bool split = su >= 0;
   if (MODE == 0 && (*n_out + 31) / 32 > 3) {
-    // whole tile in one workgroup (half 0 of a split grid is workgroup tb)
+    // whole tile in one workgroup (half 0 of a split unit is workgroup tb)
     if (half == 0)
       gemm_tile_many_outliers(sm, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, Y);
     return;
@@ -519,16 +528,20 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nr, last, wm0, wn0, mp, lane);
 
   if (MODE == 0 && split) {
-    // partial of this half, one register per pass: 512 consecutive ints
-    constexpr int kRegs = TI * TJ * 16;
-    int32_t* mine = cpart + ((size_t)tb * 2 + half) * kRegs * NT + threadIdx.x;
-    const int32_t* other = cpart + ((size_t)tb * 2 + (half ^ 1)) * kRegs * NT + threadIdx.x;
+    // partial of this half, four registers per pass: each lane stores 16
+    // bytes, each wave 1 KiB contiguous
+    constexpr int kQuads = TI * TJ * 4;
+    v4i* mine = reinterpret_cast<v4i*>(cpart) + ((size_t)su * 2 + half) * kQuads * NT + threadIdx.x;
+    const v4i* other =
+        reinterpret_cast<const v4i*>(cpart) + ((size_t)su * 2 + (half ^ 1)) * kQuads * NT + threadIdx.x;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mine[((i * TJ + j) * 16 + r) * NT] = acc[i][j][r];
+        for (int q = 0; q < 4; ++q)
+          mine[((i * TJ + j) * 4 + q) * NT] =
+              v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     // the flag lives in stage (nr+3) % NBUF, free since the loop's last
     // barrier and overwritten by the epilogue only after its own barrier
     int* s_first = reinterpret_cast<int*>(&sm.a[(nr + 3) % NBUF][0]);
@@ -536,7 +549,7 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     __syncthreads();  // ... and every other thread's
     if (threadIdx.x == 0) {
       __threadfence();  // the partial is visible device-wide before the count
-      const int first = atomicAdd(&ctr[tb], 1) == 0;
+      const int first = atomicAdd(&ctr[su], 1) == 0;
       if (!first) __threadfence();  // and the other half's is seen after it
       *s_first = first;
     }
@@ -547,7 +560,11 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] += other[((i * TJ + j) * 16 + r) * NT];
+        for (int q = 0; q < 4; ++q) {
+          const v4i o = other[((i * TJ + j) * 4 + q) * NT];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += o[e];
+        }
   }
 
   if (MODE == 1) {
@@ -621,23 +638,27 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
-                               int32_t* cpart, int32_t* ctr, hipStream_t s, hipEvent_t e0,
-                               hipEvent_t e1) {
+                               int nsplit, int32_t* cpart, int32_t* ctr, hipStream_t s,
+                               hipEvent_t e0, hipEvent_t e1) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int split = (C == nullptr && cpart != nullptr) ? 1 : 0;
   if (C != nullptr)
     hipExtLaunchKernelGGL(k_gemm_prefill<1>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
                           K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C, 0, nullptr, nullptr);
   else
-    hipExtLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles * (split + 1)), dim3(NT), 0, s, e0, e1, 0,
-                          Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C, split,
+    hipExtLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles + nsplit), dim3(NT), 0, s, e0, e1, 0,
+                          Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C, nsplit,
                           cpart, ctr);
   return hipGetLastError();
 }
 
-bool gemm_prefill_split(int M, int N, int ldk) {
+int gemm_prefill_nsplit(int M, int N, int ldk, int n_cu) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  return tiles <= 128 && ldk / kTileK >= 32;
+  if (ldk / kTileK < 32 || n_cu <= 0) return 0;  // short K: the exchange would not pay
+  // Every tile split when the tiles fill at most half of the CUs (one
+  // workgroup per CU).  Splitting only the tiles of a partly filled last
+  // round measured no faster: the exchange of the int32 partials (HBM-bound
+  // when all the split units end together) costs about what it saves.
+  return 2 * tiles <= n_cu ? tiles : 0;
 }
 
 }  // namespace i8mm

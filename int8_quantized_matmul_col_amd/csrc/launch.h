@@ -32,16 +32,17 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
                              hipStream_t s);
 // Prefill tile GEMM: int8 MFMA over K, then fp16 MFMA over the outlier slice,
 // fused dequant epilogue (Y), or int32 accumulators only (C).
-// cpart / ctr (Y only; null = no split): the K range split over two
-// workgroups per tile, int32 partials in cpart (2 * tiles * 256*256 ints),
-// per-tile counters ctr (tiles ints, zero on entry: the row pass zeroes them).
+// nsplit (Y only; 0 = none): the last nsplit tiles are computed by two
+// workgroups each, splitting K; int32 partials in cpart (2 * nsplit *
+// 256*256 ints), counters ctr (nsplit ints, zero on entry: the row pass of
+// the same call zeroes them).
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
-                               int32_t* cpart, int32_t* ctr, hipStream_t s,
+                               int nsplit, int32_t* cpart, int32_t* ctr, hipStream_t s,
                                hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
-// Whether the GEMM splits K for this shape (few tiles, long K).
-bool gemm_prefill_split(int M, int N, int ldk);
+// How many tiles the GEMM splits for this shape on a GPU of n_cu CUs.
+int gemm_prefill_nsplit(int M, int N, int ldk, int n_cu);
 // e0/e1 (optional) are stamped by the GEMM dispatch itself: start and end of
 // that kernel, for profiling.
 // Decode (M <= 16): one streaming pass over Wq, outliers handled inline.

@@ -527,15 +527,16 @@ __host__ __device__ inline int olist_cap(int ldk) {
   return ldk < room ? ldk : room;
 }
 
-// Row group (of 4 rows) of row block rb in the one-wave-per-row form: with a
-// multiple of 128 row blocks, the groups of column-absmax chunk c (16 groups
-// of 64 rows) go to blocks on XCD c % 8, the XCD that read those rows in the
+// Row group (of RPB rows) of row block rb: with a multiple of 8*G row blocks
+// (G = 64/RPB groups per column-absmax chunk of 64 rows), the groups of chunk
+// c go to blocks on XCD c % 8, the XCD that read those rows in the
 // column-absmax pass, so that the rows are re-read from its L2.
+template <int RPB>
 __device__ __forceinline__ int row_group_of(int rb, int n_row_blocks) {
-  static_assert(kRowChunk == 64, "16 row groups of 4 rows per column-absmax chunk");
-  if (n_row_blocks % 128 != 0) return rb;
+  constexpr int G = kRowChunk / RPB;
+  if (n_row_blocks % (8 * G) != 0) return rb;
   const int x = rb & 7, q = rb >> 3;
-  return 16 * (8 * (q >> 4) + x) + (q & 15);
+  return G * (8 * (q / G) + x) + (q % G);
 }
 constexpr int kWoRows = 16;
 constexpr int kRowBlocks = 2048;  // row blocks of the one-wave-per-row form
@@ -561,7 +562,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(
   const int rl = (wave % WPR) * 64 + lane;   // lane index within the row
   const int nch = ldk / 8;
   const int mstride = n_row_blocks * RPB;
-  int m = (WPR == 1 && rb >= 0 ? row_group_of(rb, n_row_blocks) : rb) * RPB + wave / WPR;
+  int m = (rb >= 0 ? row_group_of<RPB>(rb, n_row_blocks) : rb) * RPB + wave / WPR;
   // the block's first row is loaded before the mask prefix, so the two
   // memory latencies overlap
   uint4 ha[CPL > 0 ? CPL : 1];
@@ -800,10 +801,14 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
                              int32_t* out_idx, const int8_t* Wq, const float* w_scale, int N,
                              uint16_t* WO, int32_t* zero_ctr, int n_zero, hipStream_t s) {
   const int vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-  const bool few_rows = M <= 256;  // whole block per row keeps the GPU busy
-  const int wpr = few_rows ? 4 : 1;
-  // a wave per row (blocks loop over the rows only beyond 4 * kRowBlocks)
-  const int n_row_blocks = few_rows ? M : min((M + 3) / 4, kRowBlocks);
+  // a whole block per row for few rows (keeps the GPU busy) and for rows too
+  // long for one wave's registers but not for four waves' (so the row is
+  // read once); otherwise a wave per row.  Blocks loop over the rows only
+  // beyond kRowBlocks blocks.
+  const bool few_rows = M <= 256;
+  const bool long_rows = vec && (ldk / 8 + 63) / 64 > 16 && (ldk / 8 + 255) / 256 <= 8;
+  const int wpr = (few_rows || long_rows) ? 4 : 1;
+  const int n_row_blocks = wpr == 4 ? min(M, kRowBlocks) : min((M + 3) / 4, kRowBlocks);
   const int n_wo_blocks = WO != nullptr ? (N + kWoRows - 1) / kWoRows : 0;
   const size_t lds = (size_t)2 * (ldk / 32) * sizeof(uint32_t) +
                      (WO != nullptr || XO != nullptr ? (size_t)olist_cap(ldk) * sizeof(int) : 0);

@@ -41,6 +41,7 @@ SHAPES = [
     (40, 96, 520, 90, 0.5),        # |O| close to K
     (300, 2112, 520, 7, 6.0),      # K split over two workgroups per tile, odd step count
     (260, 2048, 300, 2, 0.0),      # split grid with every column an outlier
+    (300, 9000, 64, 5, 6.0),       # rows too long for one wave: a block per row
 ]
 
 

@@ -32,7 +32,7 @@ constexpr int kRowChunk = kColmaxRowsPerChunk;
 // grid = ceil(ldk/512) column blocks x ceil(M/kRowChunk) row chunks.  Workgroups
 // go round-robin to the 8 XCDs; when the chunk count is a multiple of 8,
 // chunk c is read only by workgroups on XCD c % 8 (each XCD reads whole rows,
-// which its L2 then holds for the row pass); otherwise column block fastest.
+// the same rows the row pass reads there); otherwise column block fastest.
 // Block 256 = 64 column lanes x 4 row lanes; each lane reads 8
 // consecutive columns (16 bytes) of kRowChunk/4 rows of the chunk, all loads issued
 // before use.  A wave reads one 1 KiB row segment per load instruction.
@@ -530,7 +530,9 @@ __host__ __device__ inline int olist_cap(int ldk) {
 // Row group (of RPB rows) of row block rb: with a multiple of 8*G row blocks
 // (G = 64/RPB groups per column-absmax chunk of 64 rows), the groups of chunk
 // c go to blocks on XCD c % 8, the XCD that read those rows in the
-// column-absmax pass, so that the rows are re-read from its L2.
+// column-absmax pass.  (Measured faster in both passes; the L2 is not kept
+// across kernels, the row pass fetches all of X again, so the gain is in the
+// locality of each XCD's reads, not in L2 hits.)
 template <int RPB>
 __device__ __forceinline__ int row_group_of(int rb, int n_row_blocks) {
   constexpr int G = kRowChunk / RPB;

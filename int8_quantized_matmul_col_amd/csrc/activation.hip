@@ -16,6 +16,8 @@
 // rebuilds the exclusive prefix count of the mask words in LDS, so a column's
 // slot in the compacted slices is prefix[word] + popcount of the lower bits:
 // no separate scan launch and no global O list is needed by the consumers.
+// For a few rows (M <= 16) k_activation_small does the mask and the codes in
+// one launch.
 #include "device_common.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -513,11 +515,12 @@ __device__ __forceinline__ void quant_row_stream(const uint16_t* __restrict__ X,
 
 // Row pass.  grid = row blocks followed by W_O blocks (16 weight rows each;
 // only when WO != nullptr): the row blocks take the machine first, the small
-// gathers fill the slots their tail frees.  WPR = waves per row: 1 (a wave per row, 4
-// rows per block and pass, the blocks looping over the rows) or 4 (the whole
-// block on one row, for few rows).  CPL = 8-column chunks per lane held in
-// registers between the absmax and the quantize passes (0: re-read the row
-// from L1/L2 instead, for long rows).
+// gathers fill the slots their tail frees.  WPR = waves per row: 1 (a wave
+// per row, 4 rows per block and pass, the blocks looping over the rows) or 4
+// (the whole block on one row: few rows, or rows too long for one wave's
+// registers).  CPL = 8-column chunks per lane held in registers between the
+// absmax and the quantize passes (0: re-read the row from L1/L2 instead, for
+// rows that are unaligned or too long for any register form).
 // Dynamic LDS: 2*nw words plus the O list, olist_cap(ldk) entries: every
 // column while the whole stays within 64 KiB (ldk up to ~14.5K, so that even
 // |O| = K is gathered through LDS); beyond that, larger |O| falls back to

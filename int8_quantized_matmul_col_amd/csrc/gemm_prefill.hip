@@ -15,17 +15,22 @@
 // contiguous: each wave load instruction reads 1 KiB of whole cache lines.
 // Loads go to registers (three rotating one-step buffers, so a load has two
 // steps to land) and from there to LDS with swizzled ds_write_b128.  Five LDS
-// stages: the one computed, the next one (its first fragments are read before
-// the barrier ending the current step), the one being written, and two that
-// stay free for the epilogue.  One barrier per step.
+// stages, each written three steps before it is computed: the one computed,
+// the next one (its first fragments are read before the current step ends),
+// the one written last step, the one being written, and one more, so that a
+// workgroup barrier is needed only after every second step; after the loop
+// the last two int8 stages are free for the epilogue.
 //
 // The outlier slice (|O| rounded up to 32 fp16 columns: 64 bytes per row per
 // step, the same byte shape as an int8 step) is appended to the same
 // pipeline as extra steps on v_mfma_f32_32x32x16_f16.  With at most three
 // such steps their operands are prefetched by the int8 loop and the fp16
 // products are added in the epilogue; with more, the int32 accumulators are
-// rescaled to fp32 in place and the pipeline continues over the fp16 steps
-// (out of line).  |O| is read on the device: no host synchronisation.
+// rescaled to fp32 and a loop of its own runs the fp16 steps (out of line).
+// |O| is read on the device: no host synchronisation.
+//
+// With few tiles (at most half as many as CUs) each tile is computed by two
+// workgroups that split K and exchange int32 partials (see k_gemm_prefill).
 //
 // MFMA operand convention: lane l supplies row (l%32) of its operand and 16
 // bytes of K; both fragments use the same K mapping, so the pairing of K

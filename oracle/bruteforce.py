@@ -16,7 +16,7 @@ numpy oracle (``int8mm_ref``) independently:
 from __future__ import annotations
 
 from fractions import Fraction
-from typing import List, Sequence
+from typing import List, Optional, Sequence
 
 Q_MAX = 127
 
@@ -80,9 +80,11 @@ def bf_prepare_weight(W: Sequence[Sequence[float]]):
 
 
 def bf_int8_matmul(X: Sequence[Sequence[float]], Wq: List[List[int]],
-                   a_w: List[Fraction], t: float):
+                   a_w: List[Fraction], t: float,
+                   bias: Optional[Sequence[float]] = None):
     """Returns a dict with mask, O, a_x, Xq, W_O (fp16-rounded rationals,
-    [|O|][N]), C (ints) and Y_exact (rationals) and Y16 (fp16-rounded)."""
+    [|O|][N]), C (ints) and Y_exact (rationals) and Y16 (fp16-rounded).
+    ``bias`` (fp16 values, [N]) is added exactly to Y_exact."""
     Xf = [[Fraction(v) for v in row] for row in X]
     M = len(Xf)
     K = len(Xf[0]) if M else len(Wq[0]) if Wq else 0
@@ -106,6 +108,8 @@ def bf_int8_matmul(X: Sequence[Sequence[float]], Wq: List[List[int]],
         for n in range(N):
             y = Fraction(C[m][n]) * a_x[m] * a_w[n] / (Q_MAX * Q_MAX)
             y += sum((Xf[m][k] * W_O[j][n] for j, k in enumerate(O)), Fraction(0))
+            if bias is not None:
+                y += Fraction(bias[n])
             row.append(y)
         Y_exact.append(row)
     Y16 = [[to_f16(y) for y in row] for row in Y_exact]

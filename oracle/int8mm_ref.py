@@ -32,13 +32,15 @@ design notes):
   prepared weight keeps only int8 values and fp32 scales, as with
   ``has_fp16_weights=False`` on the per-channel page;
 * the dequant scale is fp32(a_x*a_w)/16129, the merge fp32(fp32(C)*s + Y_O),
-  rounded once to fp16 (overflow to +-inf as IEEE does).
+  rounded once to fp16 (overflow to +-inf as IEEE does);
+* a linear layer's bias (fp16 b [N]) is added in fp32 after the merge, before
+  that one rounding.
 """
 
 from __future__ import annotations
 
 import math
-from typing import Dict, Tuple
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 
@@ -163,24 +165,32 @@ def outlier_gemm_ref(X_O: np.ndarray, W_O: np.ndarray, N: int) -> np.ndarray:
     return X_O.astype(np.float32) @ W_O.astype(np.float32)
 
 
-def epilogue_ref(C: np.ndarray, a_x: np.ndarray, a_w: np.ndarray, Y_O: np.ndarray) -> np.ndarray:
+def epilogue_ref(C: np.ndarray, a_x: np.ndarray, a_w: np.ndarray, Y_O: np.ndarray,
+                 bias: Optional[np.ndarray] = None) -> np.ndarray:
     """Dequantize and merge: s = fp32(a_x[m]*a_w[n]) / 16129,
-    Y = fp16( fp32( fp32(C)*s ) + Y_O ), each step rounded in fp32.
-    ("PyTorch 2.9 supports LLM.int8()", section 3: the two parts are merged.)
+    Y = fp16( fp32( fp32( fp32(C)*s ) + Y_O ) + b[n] ), each step rounded in
+    fp32, the bias term (fp16 b [N]) only when given.
+    ("PyTorch 2.9 supports LLM.int8()", section 3: the two parts are merged;
+    its ``Linear8bitLt`` example carries the layer's bias, added here after
+    the merge and before the single rounding to fp16.)
     """
     s = (a_x.astype(np.float32)[:, None] * a_w.astype(np.float32)[None, :]) / np.float32(Q_MAX * Q_MAX)
     with np.errstate(over="ignore"):
         y = C.astype(np.float32) * s
         y = y + Y_O.astype(np.float32)
+        if bias is not None:
+            y = y + np.asarray(bias, np.float16).astype(np.float32)[None, :]
         return y.astype(np.float16)
 
 
 def int8_matmul_ref(X16: np.ndarray, Wq: np.ndarray, a_w: np.ndarray,
-                    threshold: float = 6.0, stages: bool = False):
+                    threshold: float = 6.0, stages: bool = False,
+                    bias: Optional[np.ndarray] = None):
     """The whole decomposed matmul, step by step.
 
     ``Wq`` [N][K] int8 and ``a_w`` [N] fp32 are the prepared weight.
     ``threshold`` is taken as an fp32 value (the boundary passes a float).
+    ``bias`` (fp16 [N], optional) is the linear layer's bias.
     Returns Y float16 [M][N], or (Y, dict of every intermediate) if
     ``stages``.
     """
@@ -191,12 +201,15 @@ def int8_matmul_ref(X16: np.ndarray, Wq: np.ndarray, a_w: np.ndarray,
     M, K = X16.shape
     N = Wq.shape[0]
     assert Wq.shape == (N, K), (Wq.shape, (N, K))
+    if bias is not None:
+        bias = np.asarray(bias, np.float16)
+        assert bias.shape == (N,), (bias.shape, N)
     mask, O, colmax = outlier_mask_ref(X16, t)
     Xq, a_x = quantize_activation_ref(X16, mask)
     X_O, W_O = outlier_slices_ref(X16, Wq, a_w, O)
     C = int8_gemm_ref(Xq, Wq)
     Y_O = outlier_gemm_ref(X_O, W_O, N)
-    Y = epilogue_ref(C, a_x, a_w, Y_O)
+    Y = epilogue_ref(C, a_x, a_w, Y_O, bias)
     if not stages:
         return Y
     return Y, dict(mask=mask, O=O, colmax=colmax, Xq=Xq, a_x=a_x, X_O=X_O,
@@ -204,14 +217,20 @@ def int8_matmul_ref(X16: np.ndarray, Wq: np.ndarray, a_w: np.ndarray,
 
 
 def tolerance_bound(X16: np.ndarray, Wq: np.ndarray, a_w: np.ndarray,
-                    rel: float = 1e-2, abs_: float = 1e-3) -> np.ndarray:
-    """Per-element bound on |Y_gpu - Y_oracle|: rel*(|X| |W_hat|^T)[m, n] + abs_.
+                    rel: float = 1e-2, abs_: float = 1e-3,
+                    bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Per-element bound on |Y_gpu - Y_oracle|: rel*(|X| |W_hat|^T)[m, n] + abs_,
+    plus 2^-10 |b[n]| with a bias (two fp16 ulps at the bias' magnitude: the
+    terms are summed in another order before the one rounding to fp16).
 
     W_hat = Wq * a_w / 127 is the dequantized weight; the product of absolute
     values is taken in float64.
     """
     W_hat = Wq.astype(np.float64) * (a_w.astype(np.float64)[:, None] / Q_MAX)
-    return rel * (np.abs(X16.astype(np.float64)) @ np.abs(W_hat).T) + abs_
+    tol = rel * (np.abs(X16.astype(np.float64)) @ np.abs(W_hat).T) + abs_
+    if bias is not None:
+        tol = tol + 2.0 ** -10 * np.abs(np.asarray(bias, np.float16).astype(np.float64))[None, :]
+    return tol
 
 
 def fp16_ulp(y: np.ndarray) -> np.ndarray:

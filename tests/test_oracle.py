@@ -117,14 +117,15 @@ def test_prepare_weight_per_channel():
 # ---------------------------------------------------------------- brute force
 
 
-def _compare_with_bruteforce(X, W, t):
+def _compare_with_bruteforce(X, W, t, bias=None):
     Wq, a_w = ref.prepare_weight_ref(W)
     bwq, baw = bf.bf_prepare_weight(W.astype(np.float64).tolist())
     assert np.array_equal(Wq.astype(np.int64), np.array(bwq, np.int64).reshape(Wq.shape))
     assert [Fraction(float(v)) for v in a_w] == baw
-    Y, st = ref.int8_matmul_ref(X, Wq, a_w, t, stages=True)
+    Y, st = ref.int8_matmul_ref(X, Wq, a_w, t, stages=True, bias=bias)
     b = bf.bf_int8_matmul(X.astype(np.float64).tolist(), [list(map(int, r)) for r in Wq],
-                          [Fraction(float(v)) for v in a_w], t)
+                          [Fraction(float(v)) for v in a_w], t,
+                          None if bias is None else bias.astype(np.float64).tolist())
     M, K = X.shape
     N = W.shape[0]
     assert st["mask"].tolist() == b["mask"]
@@ -176,6 +177,55 @@ def test_bruteforce_random_small(seed):
     W = (rng.standard_normal((N, K)) * rng.choice([0.02, 1.0, 30.0])).astype(np.float16)
     t = [0.0, 2.0, 6.0, math.inf][seed % 4]
     _compare_with_bruteforce(X, W, t)
+
+
+def test_bruteforce_4x8x4_with_bias():
+    # the 4x8x4 case above with a bias per output channel: magnitudes both
+    # below and far above the matmul term, one negative, one exact zero
+    X = np.array([
+        [0.5, -1.25, 9.0, 0.75, 2.0, 6.0, -0.125, 1.0],
+        [1.0, 2.0, -0.5, -3.0, 0.25, 1.5, 0.0, -2.5],
+        [0.0, 0.0, 7.5, 0.0, 0.0, 0.0, 0.0, 0.0],
+        [3.96875, 0.078125, 1.0, -0.046875, 0.015625, 1.5, -0.078125, 2.0],
+    ], np.float16)
+    W = np.array([
+        [0.02, -0.01, 0.03, 0.0, 0.015, -0.025, 0.005, 0.01],
+        [-0.04, 0.02, 0.01, 0.03, -0.02, 0.0, 0.01, -0.005],
+        [0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0],
+        [0.1, -0.1, 0.05, -0.05, 0.025, -0.025, 0.0125, -0.0125],
+    ], np.float16)
+    bias = np.array([0.125, -3.5, 0.0, 40.0], np.float16)
+    _compare_with_bruteforce(X, W, 6.0, bias)
+    # channel 2 has an all-zero weight: Y there is the bias itself
+    Wq, a_w = ref.prepare_weight_ref(W)
+    Y = ref.int8_matmul_ref(X, Wq, a_w, 6.0, bias=bias)
+    assert np.all(Y[:, 2] == 0)
+    Y1 = ref.int8_matmul_ref(X, Wq, a_w, 6.0, bias=np.array([0, 0, 2.5, 0], np.float16))
+    assert np.all(Y1[:, 2] == np.float16(2.5))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bruteforce_random_small_with_bias(seed):
+    rng = np.random.default_rng(300 + seed)
+    M, K, N = rng.integers(1, 9), rng.integers(1, 17), rng.integers(1, 9)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    cols = rng.choice(K, rng.integers(0, min(3, K) + 1), replace=False)
+    X[:, cols] *= rng.uniform(4, 20)
+    X = X.astype(np.float16)
+    W = (rng.standard_normal((N, K)) * rng.choice([0.02, 1.0, 30.0])).astype(np.float16)
+    bias = (rng.standard_normal(N) * rng.choice([1e-3, 0.5, 50.0])).astype(np.float16)
+    t = [0.0, 2.0, 6.0, math.inf][seed % 4]
+    _compare_with_bruteforce(X, W, t, bias)
+
+
+def test_zero_bias_is_no_bias():
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((5, 40)).astype(np.float16)
+    W = (rng.standard_normal((6, 40)) * 0.1).astype(np.float16)
+    Wq, a_w = ref.prepare_weight_ref(W)
+    Y0 = ref.int8_matmul_ref(X, Wq, a_w, 1.5)
+    Y1 = ref.int8_matmul_ref(X, Wq, a_w, 1.5, bias=np.zeros(6, np.float16))
+    assert np.array_equal(Y0, Y1)
 
 
 def test_round_to_binary_matches_hardware_casts():

@@ -68,16 +68,34 @@ def _outlier_weight_not_dequantized(X16, Wq, a_w, O):
     return X_O, Wq[:, O].astype(np.float16).T.copy()
 
 
-def _epilogue_single_127(C, a_x, a_w, Y_O):
+def _b32(bias):
+    return 0 if bias is None else np.asarray(bias, np.float16).astype(np.float32)[None, :]
+
+
+def _epilogue_single_127(C, a_x, a_w, Y_O, bias=None):
     s = (a_x[:, None] * a_w[None, :]).astype(np.float32) / np.float32(127)
     with np.errstate(over="ignore"):
-        return (C.astype(np.float32) * s + Y_O).astype(np.float16)
+        return (C.astype(np.float32) * s + Y_O + _b32(bias)).astype(np.float16)
 
 
-def _epilogue_wrong_sign(C, a_x, a_w, Y_O):
+def _epilogue_wrong_sign(C, a_x, a_w, Y_O, bias=None):
     s = (a_x[:, None] * a_w[None, :]).astype(np.float32) / np.float32(16129)
     with np.errstate(over="ignore"):
-        return (C.astype(np.float32) * s - Y_O).astype(np.float16)
+        return (C.astype(np.float32) * s - Y_O + _b32(bias)).astype(np.float16)
+
+
+def _bias_dropped(C, a_x, a_w, Y_O, bias=None):
+    return _orig["epilogue_ref"](C, a_x, a_w, Y_O, None)
+
+
+def _bias_sign(C, a_x, a_w, Y_O, bias=None):
+    nb = None if bias is None else -np.asarray(bias, np.float16)
+    return _orig["epilogue_ref"](C, a_x, a_w, Y_O, nb)
+
+
+def _bias_reversed_index(C, a_x, a_w, Y_O, bias=None):
+    rb = None if bias is None else np.asarray(bias, np.float16)[::-1].copy()
+    return _orig["epilogue_ref"](C, a_x, a_w, Y_O, rb)
 
 
 def _gemm_transposed_k(Xq, Wq, chunk=2048):
@@ -96,6 +114,9 @@ MUTATIONS = {
     "dequant_by_127_not_127sq": ("epilogue_ref", _epilogue_single_127),
     "outlier_term_sign": ("epilogue_ref", _epilogue_wrong_sign),
     "gemm_wrong_k_index": ("int8_gemm_ref", _gemm_transposed_k),
+    "bias_dropped": ("epilogue_ref", _bias_dropped),
+    "bias_wrong_sign": ("epilogue_ref", _bias_sign),
+    "bias_wrong_index": ("epilogue_ref", _bias_reversed_index),
 }
 
 
@@ -112,7 +133,10 @@ def _run_pins():
         ("error_bound", pins.test_error_bound_against_exact_product, ()),
         ("exact_integer", pins.test_exact_integer_example, ()),
         ("strict", pins.test_strict_threshold_comparison, ()),
-    ] + [(f"bf_random_{s}", pins.test_bruteforce_random_small, (s,)) for s in range(6)]
+        ("bf_bias_4x8x4", pins.test_bruteforce_4x8x4_with_bias, ()),
+    ] + [(f"bf_random_{s}", pins.test_bruteforce_random_small, (s,)) for s in range(6)] + [
+        (f"bf_bias_random_{s}", pins.test_bruteforce_random_small_with_bias, (s,))
+        for s in range(4)]
     for name, fn, args in checks:
         try:
             with np.errstate(all="ignore"):

@@ -133,6 +133,24 @@ INT8MM_API int int8_matmul(const int8mm_half* X, int64_t M, int64_t K,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * int8_linear -- the forward of an 8-bit linear layer with a bias
+ * ("PyTorch 2.9 supports LLM.int8()", the Linear8bitLt replacement example:
+ * an nn.Linear, bias included, swapped for an 8-bit layer that keeps no fp16
+ * weight):
+ *
+ *     Y[m][n] = fp16( dequant(C)[m][n] + (X_O . W_O)[m][n] + bias[n] )
+ *
+ * the bias added in fp32 before the single rounding to fp16.  Same kernels,
+ * arguments, workspace and errors as int8_matmul, plus:
+ *   bias      [N]      float16, or NULL (then the call is int8_matmul).
+ * K == 0: Y[m][n] = bias[n] (0 without a bias).
+ */
+INT8MM_API int int8_linear(const int8mm_half* X, int64_t M, int64_t K,
+                const int8_t* Wq, const float* w_scale, int64_t N,
+                const int8mm_half* bias, float threshold, int8mm_half* Y,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * int8_matmul_stages -- the same kernels as int8_matmul for this shape, with
  * every intermediate of the method exposed (for verification).  Every output
  * pointer is optional (NULL = not wanted).  When C is given the matmul kernel

@@ -9,6 +9,11 @@ Python binding over it, with torch used only for device memory and streams.
     import int8_quantized_matmul_col_amd as mm
     Wq, w_scale = mm.int8_prepare_weight(W)          # once per weight
     Y = mm.int8_matmul(X, Wq, w_scale, threshold=6.0)
+    Y = mm.int8_linear(X, Wq, w_scale, bias)          # with a layer's bias
+
+``Int8Linear`` wraps the same calls as a torch module (forward only), and
+``replace_linear_with_int8`` swaps the fp16 ``nn.Linear`` layers of a model
+for it.
 """
 
 from .binding import (  # noqa: F401
@@ -16,6 +21,7 @@ from .binding import (  # noqa: F401
     INT8MM_DECODE_MAX_M,
     INT8MM_MAX_K,
     Int8mmError,
+    int8_linear,
     int8_matmul,
     int8_matmul_profiled,
     int8_matmul_stages,
@@ -29,3 +35,4 @@ from .binding import (  # noqa: F401
     load,
     workspace_for,
 )
+from .linear import Int8Linear, replace_linear_with_int8  # noqa: F401

@@ -39,6 +39,8 @@ SIGNATURES = {
     "int8_matmul_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "int8_matmul": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P,
                                    ctypes.c_size_t, _P]),
+    "int8_linear": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_float, _P, _P,
+                                   ctypes.c_size_t, _P]),
     "int8_matmul_profiled": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P,
                                             ctypes.c_size_t, _P, _P, _P]),
     "int8_matmul_stages": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float,
@@ -199,6 +201,36 @@ def int8_matmul(X, Wq, w_scale, threshold: float = DEFAULT_THRESHOLD, out=None, 
     st = lib.int8_matmul(_ptr(X), M, K, _ptr(Wq), _ptr(w_scale), N, float(threshold), _ptr(Y),
                          _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check("int8_matmul", st)
+    return Y
+
+
+def int8_linear(X, Wq, w_scale, bias=None, threshold: float = DEFAULT_THRESHOLD, out=None,
+                workspace=None):
+    """Y = int8_matmul(X) + bias: the forward of an 8-bit linear layer.
+    X float16 [M][K], the prepared weight (Wq, w_scale), bias float16 [N] or
+    None.  Returns float16 [M][N]."""
+    import torch
+    lib = load()
+    _require(X, torch.float16, "X")
+    dev = X.device
+    _require(Wq, torch.int8, "Wq", dev)
+    _require(w_scale, torch.float32, "w_scale", dev)
+    M, K = X.shape
+    N = w_scale.numel()
+    if Wq.numel() != int8_weight_bytes(N, K):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, "
+                         f"w_scale {tuple(w_scale.shape)}")
+    if bias is not None:
+        _require(bias, torch.float16, "bias", dev)
+        if bias.numel() != N:
+            raise ValueError(f"bias has {bias.numel()} entries, expected {N}")
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
+    if out is not None:
+        _require(Y, torch.float16, "out", dev)
+    ws = workspace if workspace is not None else workspace_for(M, K, N, dev)
+    st = lib.int8_linear(_ptr(X), M, K, _ptr(Wq), _ptr(w_scale), N, _ptr(bias), float(threshold),
+                         _ptr(Y), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check("int8_linear", st)
     return Y
 
 

@@ -773,6 +773,15 @@ __global__ void k_zero_half(uint16_t* __restrict__ Y, int64_t count) {
     Y[i] = 0;
 }
 
+// Y[m][n] = bias[n]: the whole output of an empty contraction with a bias.
+__global__ void k_bias_rows(const uint16_t* __restrict__ bias, int64_t M, int64_t N,
+                            uint16_t* __restrict__ Y) {
+  const int64_t count = M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * blockDim.x)
+    Y[i] = bias[i % N];
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_colmax_partial(const uint16_t* X, int M, int K, int ldk, uint16_t* part,
@@ -858,6 +867,15 @@ hipError_t launch_activation_small(const uint16_t* X, int M, int K, int ldk, flo
   else if (cpt <= 4) AS(4);
   else AS(8);
 #undef AS
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_rows(const uint16_t* bias, int64_t M, int64_t N, uint16_t* Y,
+                            hipStream_t s) {
+  int64_t blocks = (M * N + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_bias_rows, dim3((unsigned)blocks), dim3(256), 0, s, bias, M, N, Y);
   return hipGetLastError();
 }
 

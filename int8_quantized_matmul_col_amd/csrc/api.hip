@@ -100,7 +100,8 @@ struct Outputs {
 
 int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* w_scale, int64_t N,
         float threshold, const Outputs& out, bool stages, void* ws, size_t ws_bytes,
-        hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
+        hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+        const uint16_t* bias = nullptr) {
   int st = check_shape(M, K, N);
   if (st != INT8MM_OK) return st;
   if (isnan(threshold) || threshold < 0.0f) return INT8MM_EINVAL;
@@ -131,6 +132,8 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
     if (out.C) {
       if ((e = i8mm::launch_zero_half(reinterpret_cast<uint16_t*>(out.C), 2 * M * N, s)) != hipSuccess)
         return hip_fail(e);
+    } else if (out.Y && bias) {
+      if ((e = i8mm::launch_bias_rows(bias, M, N, out.Y, s)) != hipSuccess) return hip_fail(e);
     } else if (out.Y) {
       if ((e = i8mm::launch_zero_half(out.Y, M * N, s)) != hipSuccess) return hip_fail(e);
     }
@@ -184,12 +187,12 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
   uint16_t* Y = out.C ? nullptr : out.Y;
   if (out.C == nullptr && Y == nullptr) return INT8MM_OK;
   if (L.decode)
-    e = i8mm::launch_gemm_decode(xq, Wq, m, n, k, ldk, xs, w_scale, X, bits, Y, out.C, s, ev_start,
-                                 ev_stop);
+    e = i8mm::launch_gemm_decode(xq, Wq, m, n, k, ldk, xs, w_scale, X, bits, bias, Y, out.C, s,
+                                 ev_start, ev_stop);
   else
-    e = i8mm::launch_gemm_prefill(xq, Wq, m, n, k, ldk, xs, w_scale, xo, wo, count, Y, out.C,
-                                  nsplit, nsplit ? at<int32_t>(ws, L.cpart) : nullptr, ctr, s,
-                                  ev_start, ev_stop);
+    e = i8mm::launch_gemm_prefill(xq, Wq, m, n, k, ldk, xs, w_scale, xo, wo, count, bias, Y,
+                                  out.C, nsplit, nsplit ? at<int32_t>(ws, L.cpart) : nullptr, ctr,
+                                  s, ev_start, ev_stop);
   if (e != hipSuccess) return hip_fail(e);
   return INT8MM_OK;
 }
@@ -227,6 +230,16 @@ INT8MM_API int int8_matmul(const int8mm_half* X, int64_t M, int64_t K, const int
   Outputs out;
   out.Y = Y;
   return run(X, M, K, Wq, w_scale, N, threshold, out, false, workspace, workspace_bytes, stream);
+}
+
+INT8MM_API int int8_linear(const int8mm_half* X, int64_t M, int64_t K, const int8_t* Wq,
+                           const float* w_scale, int64_t N, const int8mm_half* bias,
+                           float threshold, int8mm_half* Y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  Outputs out;
+  out.Y = Y;
+  return run(X, M, K, Wq, w_scale, N, threshold, out, false, workspace, workspace_bytes, stream,
+             nullptr, nullptr, bias);
 }
 
 INT8MM_API int int8_matmul_profiled(const int8mm_half* X, int64_t M, int64_t K, const int8_t* Wq,

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K, int ldk,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale,
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ mask_bits,
-    uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
   __shared__ uint32_t s_bits[kMaxWords];
   __shared__ int s_red[kWaves][G * 256];
   __shared__ v4i s_wslot[kSlots][G][64];  // Wq fragments of the outlier steps
@@ -261,7 +261,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
       C[(size_t)m * N + n] = csum[u];
     } else {
       const float sc = x_scale[m] * w_scale[n] * kInv127Sq;
-      Y[(size_t)m * N + n] = f2h((float)csum[u] * sc + osum[u]);
+      const float b = bias != nullptr ? h2f(bias[n]) : 0.0f;
+      Y[(size_t)m * N + n] = f2h((float)csum[u] * sc + osum[u] + b);
     }
   }
 }
@@ -269,19 +270,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
 template <int G>
 static void launch_g(dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const int8_t* Xq, const int8_t* Wq, int M, int N,
                      int K, int ldk, const float* xs, const float* ws, const uint16_t* X,
-                     const uint32_t* mb, uint16_t* Y, int32_t* C) {
+                     const uint32_t* mb, const uint16_t* bias, uint16_t* Y, int32_t* C) {
   if (C != nullptr)
     hipExtLaunchKernelGGL((k_gemm_decode<G, 1>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq, Wq, M,
-                          N, K, ldk, xs, ws, X, mb, Y, C);
+                          N, K, ldk, xs, ws, X, mb, bias, Y, C);
   else
     hipExtLaunchKernelGGL((k_gemm_decode<G, 0>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq, Wq, M,
-                          N, K, ldk, xs, ws, X, mb, Y, C);
+                          N, K, ldk, xs, ws, X, mb, bias, Y, C);
 }
 
 hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                               const float* x_scale, const float* w_scale, const uint16_t* X,
-                              const uint32_t* mask_bits, uint16_t* Y, int32_t* C, hipStream_t s,
-                              hipEvent_t e0, hipEvent_t e1) {
+                              const uint32_t* mask_bits, const uint16_t* bias, uint16_t* Y,
+                              int32_t* C, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   // Spread the 16-row groups evenly over the 256 CUs: G groups per workgroup.
   const int groups = (N + 15) / 16;
   int G = (groups + 255) / 256;
@@ -289,14 +290,14 @@ hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, 
   if (G < 1) G = 1;
   dim3 grid((groups + G - 1) / G);
   switch (G) {
-    case 1: launch_g<1>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 2: launch_g<2>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 3: launch_g<3>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 4: launch_g<4>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 5: launch_g<5>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 6: launch_g<6>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    case 7: launch_g<7>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
-    default: launch_g<8>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, Y, C); break;
+    case 1: launch_g<1>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
+    case 2: launch_g<2>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
+    case 3: launch_g<3>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
+    case 4: launch_g<4>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
+    case 5: launch_g<5>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
+    case 6: launch_g<6>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
+    case 7: launch_g<7>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
+    default: launch_g<8>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
   }
   return hipGetLastError();
 }

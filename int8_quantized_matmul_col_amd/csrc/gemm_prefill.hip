@@ -367,12 +367,14 @@ __device__ __forceinline__ void tile_of(int b, int M, int N, int& tm, int& tn) {
 // three register buffers so that each step's loads are issued two steps
 // before it is written to LDS, one barrier per step.  Kept out of line so
 // that its registers do not shape the common path's allocation.
+template <bool BIAS>
 __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
     Smem& sm, const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
     int ldk,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale,
     const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-    const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y) {
+    const int32_t* __restrict__ n_out, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ Y) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm0 = (wave >> 2) * WM, wn0 = (wave & 3) * WN;
   int tm, tn;
@@ -405,24 +407,56 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
     run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nk8, last8, wm0, wn0, mp, lane);
   }
 
-  // fp32 accumulators: fp32(C) * a_x[m] * a_w[n] / 127^2
+  // fp32 accumulators: fp32(C) * a_x[m] * a_w[n] / 127^2 (+ b[n])
   v16f yf[TI][TJ];
+  if constexpr (!BIAS) {
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const float sx = x_scale[min(m0 + wm0 + i * 32 + (lane & 31), M - 1)];
+    for (int i = 0; i < TI; ++i) {
+      const float sx = x_scale[min(m0 + wm0 + i * 32 + (lane & 31), M - 1)];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float sw = w_scale[min(n0 + wn0 + j * 32 + acc_col(r, lane), N - 1)] * kInv127Sq;
-        yf[i][j][r] = (float)acc[i][j][r] * (sx * sw);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const float sw = w_scale[min(n0 + wn0 + j * 32 + acc_col(r, lane), N - 1)] * kInv127Sq;
+          yf[i][j][r] = (float)acc[i][j][r] * (sx * sw);
+        }
+    }
   }
 
   // fp16 steps st = 0 .. nk16-1 (pipeline steps nk8 + st): step st is in
   // register buffer st % 3 and LDS stage st % 2
   wait_all();
   __syncthreads();  // every wave is done with the int8 stages
+  if constexpr (BIAS) {
+    // the tile's scales and bias go through stage NBUF-1 (the fp16 steps use
+    // stages 0 and 1): per-element global loads of the bias as well would
+    // spill registers
+    float* s_x = reinterpret_cast<float*>(&sm.a[NBUF - 1][0]);
+    float* s_w = s_x + BM;
+    float* s_b = s_w + BN;
+    if (threadIdx.x < BM) {
+      const int t = threadIdx.x;
+      s_x[t] = x_scale[min(m0 + t, M - 1)];
+      s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
+      s_b[t] = h2f(bias[min(n0 + t, N - 1)]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const float sx = s_x[wm0 + i * 32 + (lane & 31)];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
+          const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[c]);
+          const v4f b4 = *reinterpret_cast<const v4f*>(&s_b[c]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            yf[i][j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]) + b4[e];
+        }
+    }
+  }
   gload_all(b0, src, nk8, mp);
   if (nk16 > 1) gload_all(b1, src, nk8 + 1, mp);
   if (nk16 > 2) gload_all(b2, src, nk8 + 2, mp);
@@ -477,9 +511,9 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
                int ldk,
                const float* __restrict__ x_scale, const float* __restrict__ w_scale,
                const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-               const int32_t* __restrict__ n_out, uint16_t* __restrict__ Y,
-               int32_t* __restrict__ C, int nsplit, int32_t* __restrict__ cpart,
-               int32_t* __restrict__ ctr) {
+               const int32_t* __restrict__ n_out, const uint16_t* __restrict__ bias,
+               uint16_t* __restrict__ Y, int32_t* __restrict__ C, int nsplit,
+               int32_t* __restrict__ cpart, int32_t* __restrict__ ctr) {
   __shared__ Smem sm;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int nwhole = tiles - nsplit;
@@ -493,8 +527,14 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   const bool split = su >= 0;
   if (MODE == 0 && (*n_out + 31) / 32 > 3) {
     // whole tile in one workgroup (half 0 of a split unit is workgroup tb)
-    if (half == 0)
-      gemm_tile_many_outliers(sm, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, Y);
+    if (half == 0) {
+      if (bias != nullptr)
+        gemm_tile_many_outliers<true>(sm, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out,
+                                      bias, Y);
+      else
+        gemm_tile_many_outliers<false>(sm, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out,
+                                       nullptr, Y);
+    }
     return;
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -599,10 +639,12 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   const bool vec_store = (N & 7) == 0;
   float* s_x = reinterpret_cast<float*>(&sm.a[(nr + NBUF - 1) % NBUF][0]);
   float* s_w = s_x + BM;
+  float* s_b = s_w + BN;
   if (threadIdx.x < BM) {
     const int t = threadIdx.x;
     s_x[t] = x_scale[min(m0 + t, M - 1)];
     s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
+    s_b[t] = bias != nullptr ? h2f(bias[min(n0 + t, N - 1)]) : 0.0f;
   }
   wait_all();
   __syncthreads();
@@ -619,9 +661,12 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[wn0 + j * 32 + q * 8 + (lane >> 5) * 4]);
+        const int c = wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
+        const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[c]);
+        const v4f b4 = *reinterpret_cast<const v4f*>(&s_b[c]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]);
+        for (int e = 0; e < 4; ++e)
+          y[j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]) + b4[e];
       }
     for (int st = 0; st < nk16; ++st) {
       const int stg = (nr + st) % NBUF;
@@ -642,17 +687,18 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
-                               const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
-                               int nsplit, int32_t* cpart, int32_t* ctr, hipStream_t s,
-                               hipEvent_t e0, hipEvent_t e1) {
+                               const uint16_t* WO, const int32_t* n_out, const uint16_t* bias,
+                               uint16_t* Y, int32_t* C, int nsplit, int32_t* cpart, int32_t* ctr,
+                               hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (C != nullptr)
     hipExtLaunchKernelGGL(k_gemm_prefill<1>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
-                          K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C, 0, nullptr, nullptr);
+                          K, ldk, x_scale, w_scale, XO, WO, n_out, nullptr, Y, C, 0, nullptr,
+                          nullptr);
   else
     hipExtLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles + nsplit), dim3(NT), 0, s, e0, e1, 0,
-                          Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, Y, C, nsplit,
-                          cpart, ctr);
+                          Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, bias, Y, C,
+                          nsplit, cpart, ctr);
   return hipGetLastError();
 }
 

@@ -31,16 +31,17 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
                              uint16_t* WO, int32_t* zero_ctr, int n_zero,
                              hipStream_t s);
 // Prefill tile GEMM: int8 MFMA over K, then fp16 MFMA over the outlier slice,
-// fused dequant epilogue (Y), or int32 accumulators only (C).
+// fused dequant epilogue (Y, plus bias[n] when bias != nullptr), or int32
+// accumulators only (C).
 // nsplit (Y only; 0 = none): the last nsplit tiles are computed by two
 // workgroups each, splitting K; int32 partials in cpart (2 * nsplit *
 // 256*256 ints), counters ctr (nsplit ints, zero on entry: the row pass of
 // the same call zeroes them).
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
-                               const uint16_t* WO, const int32_t* n_out, uint16_t* Y, int32_t* C,
-                               int nsplit, int32_t* cpart, int32_t* ctr, hipStream_t s,
-                               hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+                               const uint16_t* WO, const int32_t* n_out, const uint16_t* bias,
+                               uint16_t* Y, int32_t* C, int nsplit, int32_t* cpart, int32_t* ctr,
+                               hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // How many tiles the GEMM splits for this shape on a GPU of n_cu CUs.
 int gemm_prefill_nsplit(int M, int N, int ldk, int n_cu);
 // e0/e1 (optional) are stamped by the GEMM dispatch itself: start and end of
@@ -48,10 +49,14 @@ int gemm_prefill_nsplit(int M, int N, int ldk, int n_cu);
 // Decode (M <= 16): one streaming pass over Wq, outliers handled inline.
 hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                               const float* x_scale, const float* w_scale, const uint16_t* X,
-                              const uint32_t* mask_bits, uint16_t* Y, int32_t* C, hipStream_t s,
-                              hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+                              const uint32_t* mask_bits, const uint16_t* bias, uint16_t* Y,
+                              int32_t* C, hipStream_t s, hipEvent_t e0 = nullptr,
+                              hipEvent_t e1 = nullptr);
 // Y[0 .. count) = 0 (K == 0 case).
 hipError_t launch_zero_half(uint16_t* Y, int64_t count, hipStream_t s);
+// Y[m][n] = bias[n] for an [M][N] Y (K == 0 case with a bias).
+hipError_t launch_bias_rows(const uint16_t* bias, int64_t M, int64_t N, uint16_t* Y,
+                            hipStream_t s);
 // Few rows (M <= 16): mask and row quantization in one launch (grid = M).
 // Applicable when activation_small_ok(); X_O optional, no W_O.
 bool activation_small_ok(const uint16_t* X, int M, int K, int ldk);

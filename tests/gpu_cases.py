@@ -33,18 +33,22 @@ def check_prepare(mm, W16: np.ndarray):
     return Wq_d, s_d, Wq_r, s_r
 
 
-def y_bounds(X16, Wq_r, s_r, Y_ref, n_out):
+def y_bounds(X16, Wq_r, s_r, Y_ref, n_out, bias=None):
     """(spec tolerance, tight bound).  The tight bound allows one fp16
     ulp of the result plus the fp32 rounding that different summation orders
-    of the |O| outlier products and the rescaled int32 term can produce."""
-    loose = ref.tolerance_bound(X16, Wq_r, s_r)
-    absprod = (loose - 1e-3) / 1e-2
-    tight = ref.fp16_ulp(Y_ref.astype(np.float64)) + (n_out + 16) * 2.0 ** -23 * absprod
+    of the |O| outlier products, the rescaled int32 term and the bias (when
+    there is one) can produce."""
+    loose = ref.tolerance_bound(X16, Wq_r, s_r, bias=bias)
+    absprod = ref.tolerance_bound(X16, Wq_r, s_r, rel=1.0, abs_=0.0)
+    mag = absprod
+    if bias is not None:
+        mag = mag + np.abs(np.asarray(bias, np.float16).astype(np.float64))[None, :]
+    tight = ref.fp16_ulp(Y_ref.astype(np.float64)) + (n_out + 16) * 2.0 ** -23 * mag
     return loose, tight
 
 
-def check_y(Y: np.ndarray, Y_ref: np.ndarray, X16, Wq_r, s_r, n_out, what="Y"):
-    loose, tight = y_bounds(X16, Wq_r, s_r, Y_ref, n_out)
+def check_y(Y: np.ndarray, Y_ref: np.ndarray, X16, Wq_r, s_r, n_out, what="Y", bias=None):
+    loose, tight = y_bounds(X16, Wq_r, s_r, Y_ref, n_out, bias)
     y = Y.astype(np.float64)
     yr = Y_ref.astype(np.float64)
     fin = np.isfinite(yr)

@@ -40,8 +40,8 @@ def header_functions():
 def test_header_declares_the_boundary():
     fns = header_functions()
     assert fns == sorted(["int8_weight_ld", "int8_weight_bytes", "int8_prepare_weight", "int8_matmul_workspace_size",
-                          "int8_matmul", "int8_matmul_stages", "int8_matmul_profiled", "int8mm_strerror",
-                          "int8mm_last_hip_error"])
+                          "int8_matmul", "int8_linear", "int8_matmul_stages", "int8_matmul_profiled",
+                          "int8mm_strerror", "int8mm_last_hip_error"])
     assert set(fns) == set(binding.SIGNATURES)
 
 
@@ -142,6 +142,26 @@ def test_matmul_empty_is_a_noop(lib):
 def test_matmul_accepts_infinite_threshold_in_validation(lib):
     # +inf passes the threshold check: the call then fails on the workspace
     assert _mm(lib, t=math.inf, ws=None) == binding.INT8MM_EWORKSPACE
+
+
+def _lin(lib, X=FAKE, M=4, K=8, Wq=FAKE, s=FAKE, N=4, b=FAKE, t=6.0, Y=FAKE, ws=FAKE_WS,
+         nbytes=1 << 30):
+    return lib.int8_linear(X, M, K, Wq, s, N, b, t, Y, ws, nbytes, None)
+
+
+def test_linear_rejects_bad_arguments(lib):
+    # the same checks as int8_matmul; a NULL bias is valid (no bias)
+    assert _lin(lib, M=-1) == binding.INT8MM_ESHAPE
+    assert _lin(lib, K=binding.INT8MM_MAX_K + 1) == binding.INT8MM_ESHAPE
+    assert _lin(lib, t=float("nan")) == binding.INT8MM_EINVAL
+    assert _lin(lib, X=None) == binding.INT8MM_EINVAL
+    assert _lin(lib, s=None) == binding.INT8MM_EINVAL
+    assert _lin(lib, Y=None) == binding.INT8MM_EINVAL
+    assert _lin(lib, Wq=FAKE + 8) == binding.INT8MM_EINVAL
+    assert _lin(lib, b=None, ws=None) == binding.INT8MM_EWORKSPACE
+    assert _lin(lib, ws=FAKE_WS + 16) == binding.INT8MM_EWORKSPACE
+    assert _lin(lib, M=0) == binding.INT8MM_OK
+    assert _lin(lib, N=0, b=None) == binding.INT8MM_OK
 
 
 def test_stages_rejects_bad_arguments(lib):

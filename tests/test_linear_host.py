@@ -1,0 +1,63 @@
+"""Host-side checks of the 8-bit linear layer's module logic (no GPU): which
+layers the replacement policy swaps, what the layer keeps before its first
+use, and that it refuses to run without a GPU instead of falling back."""
+
+import pytest
+import torch
+
+import int8_quantized_matmul_col_amd as mm
+
+
+def _net():
+    net = torch.nn.Sequential()
+    net.add_module("small", torch.nn.Linear(64, 128))
+    block = torch.nn.Sequential()
+    block.add_module("q_proj", torch.nn.Linear(1024, 1024, bias=False))
+    block.add_module("lm_head", torch.nn.Linear(1024, 32))
+    net.add_module("block", block)
+    net.add_module("f32", torch.nn.Linear(1024, 16))
+    net.add_module("lm_head", torch.nn.Linear(16, 8))
+    for name in ("small", "block", "lm_head"):
+        getattr(net, name).half()
+    return net
+
+
+def test_replacement_policy_size_and_skip():
+    net = mm.replace_linear_with_int8(_net(), threshold=5.0, min_in_features=600,
+                                      skip_modules=("lm_head",))
+    assert type(net.small) is torch.nn.Linear            # below the size threshold
+    assert isinstance(net.block.q_proj, mm.Int8Linear)   # replaced
+    assert type(net.block.lm_head) is torch.nn.Linear    # skipped by name at any depth
+    assert type(net.f32) is torch.nn.Linear              # not float16: left alone
+    assert type(net.lm_head) is torch.nn.Linear
+    q = net.block.q_proj
+    assert q.threshold == 5.0 and q.bias is None and not q.quantized
+    assert q.in_features == 1024 and q.out_features == 1024
+
+
+def test_replacement_skips_qualified_names():
+    net = mm.replace_linear_with_int8(_net(), min_in_features=0, skip_modules=("block.q_proj",))
+    assert type(net.block.q_proj) is torch.nn.Linear
+    assert isinstance(net.block.lm_head, mm.Int8Linear)  # the default skip list is replaced
+    assert isinstance(net.small, mm.Int8Linear)
+
+
+def test_from_linear_copies_weight_and_bias():
+    lin = torch.nn.Linear(32, 48).half()
+    m = mm.Int8Linear.from_linear(lin, threshold=6.0)
+    assert torch.equal(m.weight, lin.weight) and torch.equal(m.bias, lin.bias)
+    assert m.Wq is None and m.w_scale is None
+    with pytest.raises(TypeError):
+        mm.Int8Linear.from_linear(torch.nn.Linear(4, 4))  # float32 layer
+    with pytest.raises(ValueError):
+        mm.Int8Linear(4, 4, threshold=-1.0)
+
+
+def test_forward_refuses_to_run_on_the_host():
+    m = mm.Int8Linear.from_linear(torch.nn.Linear(32, 48).half())
+    with pytest.raises(RuntimeError, match="GPU"):
+        m(torch.zeros(2, 32, dtype=torch.float16))
+    with pytest.raises(TypeError):
+        m(torch.zeros(2, 32))
+    with pytest.raises(ValueError):
+        m(torch.zeros(2, 31, dtype=torch.float16))

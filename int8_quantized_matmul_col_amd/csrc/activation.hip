@@ -200,29 +200,6 @@ __device__ __forceinline__ int select_outlier(const uint32_t* s_bits, const int*
 
 namespace {
 
-// |v - rint(v)| above this sends a lane to the IEEE division (quant8).
-constexpr float kTieGuard = 0.5f - 0x1p-14f;
-
-// binary16 bits of column i (0..7) of a 16-byte chunk.
-__device__ __forceinline__ uint32_t half_at(const uint4& w, int i) {
-  const uint32_t d = i < 2 ? w.x : i < 4 ? w.y : i < 6 ? w.z : w.w;
-  return (i & 1) ? (d >> 16) : (d & 0xffffu);
-}
-
-// 16-byte chunk of 8 binary16 values at row[c0], zero past K.
-__device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ row, int c0, int K,
-                                            bool vec) {
-  if (vec && c0 + 8 <= K) return *reinterpret_cast<const uint4*>(row + c0);
-  uint32_t d[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t lo = (c0 + 2 * p < K) ? row[c0 + 2 * p] : 0u;
-    const uint32_t hi = (c0 + 2 * p + 1 < K) ? row[c0 + 2 * p + 1] : 0u;
-    d[p] = lo | (hi << 16);
-  }
-  return uint4{d[0], d[1], d[2], d[3]};
-}
-
 // Bytes (or binary16 halves) of a chunk that belong to regular columns: the
 // mask bits ob (bit i = column i is an outlier) expanded to keep-masks.
 __device__ __forceinline__ uint32_t keep_bytes(uint32_t ob4) {
@@ -233,13 +210,6 @@ __device__ __forceinline__ uint32_t keep_bytes(uint32_t ob4) {
 }
 __device__ __forceinline__ uint32_t keep_halves(uint32_t ob2) {
   return ((ob2 & 1u) ? 0u : 0xffffu) | ((ob2 & 2u) ? 0u : 0xffff0000u);
-}
-
-// Two-lane unsigned 16-bit max of packed words (v_pk_max_u16).
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-  typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
-  const v2u16 m = __builtin_elementwise_max(__builtin_bit_cast(v2u16, a), __builtin_bit_cast(v2u16, b));
-  return __builtin_bit_cast(uint32_t, m);
 }
 
 // Packed |x| maxima (two 16-bit lanes) of the regular columns of a chunk.
@@ -253,49 +223,6 @@ __device__ __forceinline__ uint32_t chunk_absmax2(const uint4& w, uint32_t ob) {
     d3 &= keep_halves((ob >> 6) & 3u);
   }
   return pk_max_u16(pk_max_u16(d0, d1), pk_max_u16(d2, d3));
-}
-
-__device__ __forceinline__ uint2 pack8_i8(const int (&q)[8]) {
-  const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)q[1], (uint32_t)q[0], 0x0c0c0400u);
-  const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)q[3], (uint32_t)q[2], 0x0c0c0400u);
-  const uint32_t p45 = __builtin_amdgcn_perm((uint32_t)q[5], (uint32_t)q[4], 0x0c0c0400u);
-  const uint32_t p67 = __builtin_amdgcn_perm((uint32_t)q[7], (uint32_t)q[6], 0x0c0c0400u);
-  return uint2{__builtin_amdgcn_perm(p23, p01, 0x05040100u),
-               __builtin_amdgcn_perm(p67, p45, 0x05040100u)};
-}
-
-// Codes of the 8 columns of a chunk against the row scale a, with
-// r = RN(127/a) (0 when a == 0).  For |x| <= a the exact product x*r lies
-// within 2^-17 of the exact 127x/a, so t = rint(RN(x*r)) is the exact
-// round-half-even code wherever |x*r - t| (one fma) is at most 1/2 - 2^-14;
-// there it also equals rint of the IEEE quotient fp32(127x)/a (checked on
-// every binary16 pair 0 <= x <= a on the host).  Returns the largest such
-// deviation in *dev: above kTieGuard (about 1.5e-4 of the values) the caller
-// recomputes the chunk with quant8_exact.  Outlier columns (|x| > a) get
-// arbitrary codes here; the caller zeroes them.  Branch-free, so the chunks
-// of a row interleave.
-__device__ __forceinline__ uint2 quant8_fast(const uint4& w, float r, float* dev) {
-  int q[8];
-  float d = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x = h2f((uint16_t)half_at(w, i));
-    // RN(x*r) as an fma with a +0 addend, so it reads the binary16 operand
-    // directly (a -0 product becomes +0, which quantizes the same)
-    const float t = rintf(__builtin_fmaf(x, r, 0.0f));
-    d = fmaxf(d, fabsf(__builtin_fmaf(x, r, -t)));
-    q[i] = (int)t;
-  }
-  *dev = d;
-  return pack8_i8(q);
-}
-
-// The same codes through the IEEE division (quant_code).
-__device__ __forceinline__ uint2 quant8_exact(const uint4& w, float a) {
-  int q[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = quant_code(h2f((uint16_t)half_at(w, i)), a);
-  return pack8_i8(q);
 }
 
 // Outlier columns of one chunk of row m (mask bits ob = (word >> sh) & 0xff,

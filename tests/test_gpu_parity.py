@@ -108,6 +108,16 @@ def test_prepare_weight_ties_and_odd_shapes(lib):
     check_prepare(lib, np.zeros((4, 70), np.float16))
 
 
+@pytest.mark.parametrize("N,K", [(6, 32768), (5, 32769), (3, 40000), (9, 1001), (4, 2048)])
+def test_prepare_weight_row_lengths(lib, N, K):
+    # rows held in registers up to 32768 columns (load rounds 1 .. 16), the
+    # two-pass form beyond; K % 8 != 0 takes the element-wise loads
+    print(f"case prepare N={N} K={K}", flush=True)
+    W = workloads.make_w(N, K, N * 100003 + K, 0.02)
+    W[:, K // 3] = np.float16(-0.5)  # the absmax at a negative entry
+    check_prepare(lib, W)
+
+
 def test_empty_and_degenerate_shapes(lib):
     import torch
     mm = lib

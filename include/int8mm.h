@@ -151,6 +151,25 @@ INT8MM_API int int8_linear(const int8mm_half* X, int64_t M, int64_t K,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * int8_column_absmax -- the column maxima the outlier test compares with the
+ * threshold: colmax[k] = max_m |X[m][k]| (0 when M == 0), exact, as float16.
+ * The statistic behind choosing the threshold ("LLM.int8() notes", section
+ * 5.1: look at the activation maxima before setting it; a column is an
+ * outlier column for every t < colmax[k]).  Same kernels as the outlier
+ * detection of int8_matmul.
+ *
+ *   X         [M][K]   float16 activations (row-major).
+ *   colmax    [K]      float16 out.
+ *   workspace          >= int8_matmul_workspace_size(M, K, 0) bytes, 256-byte
+ *                      aligned (contents on entry do not matter).
+ * K == 0: nothing to do.  Errors: EINVAL (null X with M, K > 0; null colmax
+ * with K > 0), ESHAPE, EWORKSPACE, EHIP.
+ */
+INT8MM_API int int8_column_absmax(const int8mm_half* X, int64_t M, int64_t K,
+                       int8mm_half* colmax, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
  * int8_matmul_stages -- the same kernels as int8_matmul for this shape, with
  * every intermediate of the method exposed (for verification).  Every output
  * pointer is optional (NULL = not wanted).  When C is given the matmul kernel

@@ -13,7 +13,8 @@ Python binding over it, with torch used only for device memory and streams.
 
 ``Int8Linear`` wraps the same calls as a torch module (forward only), and
 ``replace_linear_with_int8`` swaps the fp16 ``nn.Linear`` layers of a model
-for it.
+for it.  ``outlier_stats`` summarizes the column maxima of an activation
+(``int8_column_absmax``) to help choose the threshold.
 """
 
 from .binding import (  # noqa: F401
@@ -21,6 +22,7 @@ from .binding import (  # noqa: F401
     INT8MM_DECODE_MAX_M,
     INT8MM_MAX_K,
     Int8mmError,
+    int8_column_absmax,
     int8_linear,
     int8_matmul,
     int8_matmul_profiled,
@@ -36,3 +38,4 @@ from .binding import (  # noqa: F401
     workspace_for,
 )
 from .linear import Int8Linear, replace_linear_with_int8  # noqa: F401
+from .stats import outlier_stats, suggest_threshold  # noqa: F401

@@ -43,6 +43,7 @@ SIGNATURES = {
                                    ctypes.c_size_t, _P]),
     "int8_matmul_profiled": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P,
                                             ctypes.c_size_t, _P, _P, _P]),
+    "int8_column_absmax": (ctypes.c_int, [_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
     "int8_matmul_stages": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float,
                                           _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, ctypes.c_size_t, _P]),
@@ -232,6 +233,28 @@ def int8_linear(X, Wq, w_scale, bias=None, threshold: float = DEFAULT_THRESHOLD,
                          _ptr(Y), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check("int8_linear", st)
     return Y
+
+
+def int8_column_absmax(X, out=None, workspace=None):
+    """colmax[k] = max_m |X[m][k]| (float16 [K], exact) of X float16 [M][K]:
+    what the outlier test compares with the threshold."""
+    import torch
+    lib = load()
+    _require(X, torch.float16, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [M][K]")
+    dev = X.device
+    M, K = X.shape
+    cm = out if out is not None else torch.empty((K,), dtype=torch.float16, device=dev)
+    if out is not None:
+        _require(cm, torch.float16, "out", dev)
+        if cm.numel() != K:
+            raise ValueError(f"out has {cm.numel()} entries, expected {K}")
+    ws = workspace if workspace is not None else workspace_for(M, K, 0, dev)
+    st = lib.int8_column_absmax(_ptr(X), M, K, _ptr(cm), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(dev))
+    _check("int8_column_absmax", st)
+    return cm
 
 
 def int8_matmul_profiled(X, Wq, w_scale, threshold: float, out, workspace, ev_start: int,

@@ -93,7 +93,8 @@ __global__ __launch_bounds__(256) void k_colmask(const uint16_t* __restrict__ X,
                                                  const uint16_t* __restrict__ part, int rc,
                                                  int M, int K, int ldk, float threshold,
                                                  uint8_t* __restrict__ mask8,
-                                                 uint32_t* __restrict__ mask_bits) {
+                                                 uint32_t* __restrict__ mask_bits,
+                                                 uint16_t* __restrict__ colmax) {
   const int cl = threadIdx.x & 63, pl = threadIdx.x >> 6;
   const int col = blockIdx.x * 64 + cl;
   uint32_t v = 0;
@@ -131,6 +132,7 @@ __global__ __launch_bounds__(256) void k_colmask(const uint16_t* __restrict__ X,
     v = max(max(s[0][cl], s[1][cl]), max(s[2][cl], s[3][cl]));
     const bool o = (col < K) && (h2f((uint16_t)v) > threshold);
     if (mask8 != nullptr && col < K) mask8[col] = o ? 1 : 0;
+    if (colmax != nullptr && col < K) colmax[col] = (uint16_t)v;
     const uint64_t b = __ballot(o);
     if (cl == 0 && blockIdx.x * 64 < ldk) {
       mask_bits[blockIdx.x * 2] = (uint32_t)b;
@@ -721,10 +723,10 @@ hipError_t launch_colmax_partial(const uint16_t* X, int M, int K, int ldk, uint1
 
 hipError_t launch_colmask(const uint16_t* X, const uint16_t* part, int rc, int M, int K,
                           int ldk, float threshold, uint8_t* mask8, uint32_t* mask_bits,
-                          hipStream_t s) {
+                          hipStream_t s, uint16_t* colmax) {
   dim3 grid((ldk + 63) / 64);
   hipLaunchKernelGGL(k_colmask, grid, dim3(256), 0, s, X, part, rc, M, K, ldk, threshold, mask8,
-                     mask_bits);
+                     mask_bits, colmax);
   return hipGetLastError();
 }
 

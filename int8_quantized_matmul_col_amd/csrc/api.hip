@@ -242,6 +242,36 @@ INT8MM_API int int8_linear(const int8mm_half* X, int64_t M, int64_t K, const int
              nullptr, nullptr, bias);
 }
 
+INT8MM_API int int8_column_absmax(const int8mm_half* X, int64_t M, int64_t K,
+                                  int8mm_half* colmax, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  int st = check_shape(M, K, 0);
+  if (st != INT8MM_OK) return st;
+  if (K == 0) return INT8MM_OK;
+  if (colmax == nullptr || (M > 0 && X == nullptr)) return INT8MM_EINVAL;
+  hipError_t e;
+  if (M == 0) {  // no rows: every column maximum is 0
+    if ((e = i8mm::launch_zero_half(colmax, K, stream)) != hipSuccess) return hip_fail(e);
+    return INT8MM_OK;
+  }
+  const Layout L = make_layout(M, K, 0);
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0 ||
+      workspace_bytes < L.total)
+    return INT8MM_EWORKSPACE;
+  const int m = (int)M, k = (int)K, ldk = (int)L.ldk;
+  uint32_t* bits = at<uint32_t>(workspace, L.bits);
+  uint16_t* part = nullptr;
+  if (!L.decode) {
+    part = at<uint16_t>(workspace, L.part);
+    if ((e = i8mm::launch_colmax_partial(X, m, k, ldk, part, stream)) != hipSuccess)
+      return hip_fail(e);
+  }
+  if ((e = i8mm::launch_colmask(X, part, L.rc, m, k, ldk, INFINITY, nullptr, bits, stream,
+                                colmax)) != hipSuccess)
+    return hip_fail(e);
+  return INT8MM_OK;
+}
+
 INT8MM_API int int8_matmul_profiled(const int8mm_half* X, int64_t M, int64_t K, const int8_t* Wq,
                                     const float* w_scale, int64_t N, float threshold,
                                     int8mm_half* Y, void* workspace, size_t workspace_bytes,

@@ -19,10 +19,11 @@ hipError_t launch_prepare_weight(const uint16_t* W, int N, int K, int ldk, int8_
 hipError_t launch_colmax_partial(const uint16_t* X, int M, int K, int ldk, uint16_t* part,
                                  hipStream_t s);
 // Reduces the partials (rc > 0) or scans X directly (part == nullptr, small
-// M) into the outlier mask: bytes mask8[K] (optional) and bits mask_bits[ldk/32].
+// M) into the outlier mask: bytes mask8[K] (optional) and bits mask_bits[ldk/32];
+// optionally the column maxima themselves, colmax[K] (|x| binary16 bits).
 hipError_t launch_colmask(const uint16_t* X, const uint16_t* part, int rc, int M, int K,
                           int ldk, float threshold, uint8_t* mask8, uint32_t* mask_bits,
-                          hipStream_t s);
+                          hipStream_t s, uint16_t* colmax = nullptr);
 // Row quantization over R, outlier compaction, |O| and the O list; optionally
 // the dequantized outlier weight rows W_O (when WO != nullptr).
 hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uint32_t* mask_bits,

@@ -41,7 +41,7 @@ def test_header_declares_the_boundary():
     fns = header_functions()
     assert fns == sorted(["int8_weight_ld", "int8_weight_bytes", "int8_prepare_weight", "int8_matmul_workspace_size",
                           "int8_matmul", "int8_linear", "int8_matmul_stages", "int8_matmul_profiled",
-                          "int8mm_strerror", "int8mm_last_hip_error"])
+                          "int8_column_absmax", "int8mm_strerror", "int8mm_last_hip_error"])
     assert set(fns) == set(binding.SIGNATURES)
 
 
@@ -162,6 +162,19 @@ def test_linear_rejects_bad_arguments(lib):
     assert _lin(lib, ws=FAKE_WS + 16) == binding.INT8MM_EWORKSPACE
     assert _lin(lib, M=0) == binding.INT8MM_OK
     assert _lin(lib, N=0, b=None) == binding.INT8MM_OK
+
+
+def test_column_absmax_rejects_bad_arguments(lib):
+    f = lib.int8_column_absmax
+    assert f(FAKE, -1, 8, FAKE, FAKE_WS, 1 << 30, None) == binding.INT8MM_ESHAPE
+    assert f(FAKE, 4, binding.INT8MM_MAX_K + 1, FAKE, FAKE_WS, 1 << 30, None) == binding.INT8MM_ESHAPE
+    assert f(None, 4, 8, FAKE, FAKE_WS, 1 << 30, None) == binding.INT8MM_EINVAL
+    assert f(FAKE, 4, 8, None, FAKE_WS, 1 << 30, None) == binding.INT8MM_EINVAL
+    assert f(FAKE, 40, 8, FAKE, None, 1 << 30, None) == binding.INT8MM_EWORKSPACE
+    assert f(FAKE, 40, 8, FAKE, FAKE_WS + 64, 1 << 30, None) == binding.INT8MM_EWORKSPACE
+    need = lib.int8_matmul_workspace_size(40, 8, 0)
+    assert f(FAKE, 40, 8, FAKE, FAKE_WS, need - 1, None) == binding.INT8MM_EWORKSPACE
+    assert f(None, 4, 0, None, None, 0, None) == binding.INT8MM_OK  # K == 0: nothing to do
 
 
 def test_stages_rejects_bad_arguments(lib):

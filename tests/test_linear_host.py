@@ -1,6 +1,7 @@
-"""Host-side checks of the 8-bit linear layer's module logic (no GPU): which
-layers the replacement policy swaps, what the layer keeps before its first
-use, and that it refuses to run without a GPU instead of falling back."""
+"""Host-side checks of the module-level helpers (no GPU): which layers the
+8-bit replacement policy swaps, what the layer keeps before its first use,
+that it refuses to run without a GPU instead of falling back, and the
+threshold suggestion from given column statistics."""
 
 import pytest
 import torch
@@ -61,3 +62,15 @@ def test_forward_refuses_to_run_on_the_host():
         m(torch.zeros(2, 32))
     with pytest.raises(ValueError):
         m(torch.zeros(2, 31, dtype=torch.float16))
+
+
+def test_suggest_threshold_from_stats():
+    stats = {"K": 1000, "n_outliers": {4.0: 40, 5.0: 11, 6.0: 10, 7.0: 3, 8.0: 0, 10.0: 0,
+                                       16.0: 0}}
+    assert mm.suggest_threshold(stats=stats, max_fp16_fraction=0.01) == 6.0
+    assert mm.suggest_threshold(stats=stats, max_fp16_fraction=0.05) == 4.0
+    assert mm.suggest_threshold(stats=stats, max_fp16_fraction=0.0) == 8.0
+    stats["n_outliers"] = {t: 999 for t in stats["n_outliers"]}
+    assert mm.suggest_threshold(stats=stats, max_fp16_fraction=0.01) == float("inf")
+    with pytest.raises(ValueError):
+        mm.suggest_threshold(stats={"K": 10, "n_outliers": {}}, candidates=(6.0,))

@@ -13,6 +13,7 @@ import pytest
 
 from oracle import int8mm_ref as ref
 import test_oracle as pins
+import test_accuracy_study as study
 
 _orig = {n: getattr(ref, n) for n in ("quantize_rows_ref", "outlier_mask_ref",
                                       "quantize_activation_ref", "outlier_slices_ref",
@@ -134,6 +135,7 @@ def _run_pins():
         ("exact_integer", pins.test_exact_integer_example, ()),
         ("strict", pins.test_strict_threshold_comparison, ()),
         ("bf_bias_4x8x4", pins.test_bruteforce_4x8x4_with_bias, ()),
+        ("accuracy_claims", study.test_accuracy_claims_on_the_oracle, ()),
     ] + [(f"bf_random_{s}", pins.test_bruteforce_random_small, (s,)) for s in range(6)] + [
         (f"bf_bias_random_{s}", pins.test_bruteforce_random_small_with_bias, (s,))
         for s in range(4)]

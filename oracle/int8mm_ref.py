@@ -19,11 +19,10 @@ weight with one row per output channel, t the outlier threshold):
   columns ("vector-wise" quantization, "LLM.int8() notes" introduction).
   Values round half to even and clamp to [-127, 127].
 * The int8 product accumulates exactly (int32 on the device), is rescaled by
-  a_x[m] * a_w[n] / 127^2, and the fp16 outlier product is added ("the
-  results are merged", "PyTorch 2.9 supports LLM.int8()", section 3).
+  a_x[m] * a_w[n] / 127^2, and the fp16 outlier product is added (the two
+  partial results are merged: "PyTorch 2.9 supports LLM.int8()", section 3).
 
-Readings where the pages are silent or garbled (each is also listed in the
-design notes):
+Readings where the pages are silent or garbled:
 
 * the outlier comparison is strict: a column is an outlier when its max |x|
   is > t (the comparison operator is lost in the page's extracted code);

@@ -34,7 +34,7 @@ def check_prepare(mm, W16: np.ndarray):
 
 
 def y_bounds(X16, Wq_r, s_r, Y_ref, n_out, bias=None):
-    """(spec tolerance, tight bound).  The tight bound allows one fp16
+    """(method tolerance, tight bound).  The tight bound allows one fp16
     ulp of the result plus the fp32 rounding that different summation orders
     of the |O| outlier products, the rescaled int32 term and the bias (when
     there is one) can produce."""

@@ -11,9 +11,10 @@ chosen modules by name, typically ``lm_head``.
 ``Int8Linear`` is that layer on this library: the weight is prepared with
 ``int8_prepare_weight`` the first time the layer runs on a GPU (or when
 ``quantize_()`` is called), after which the layer holds only the int8 weight,
-its per-channel scales and the fp16 bias; ``forward`` is one ``int8_linear``
-call.  No arithmetic of the method runs here: inputs are reshaped to 2-D and
-handed to the HIP kernels as they are.
+its per-channel scales and the fp16 bias (its state dict then carries ``Wq``
+and ``w_scale``, and loads back without re-quantizing); ``forward`` is one
+``int8_linear`` call.  No arithmetic of the method runs here: inputs are
+reshaped to 2-D and handed to the HIP kernels as they are.
 """
 
 from __future__ import annotations
@@ -88,6 +89,49 @@ class Int8Linear(torch.nn.Module):
         self.weight = None
         return self
 
+    def _load_from_state_dict(self, state_dict, prefix, local_metadata, strict, missing_keys,
+                              unexpected_keys, error_msgs):
+        # a saved 8-bit layer carries Wq and w_scale instead of the fp16
+        # weight: take them as they are (no re-quantization)
+        kq, ks, kw = prefix + "Wq", prefix + "w_scale", prefix + "weight"
+        if kq in state_dict and ks in state_dict:
+            Wq, ws = state_dict[kq], state_dict[ks]
+            ldk = (self.in_features + 63) // 64 * 64
+            Np = (self.out_features + 255) // 256 * 256
+            if tuple(Wq.shape) != (Np, ldk) or Wq.dtype != torch.int8:
+                error_msgs.append(f"{kq}: expected int8 {(Np, ldk)}, got {Wq.dtype} "
+                                  f"{tuple(Wq.shape)}")
+                return
+            if tuple(ws.shape) != (self.out_features,) or ws.dtype != torch.float32:
+                error_msgs.append(f"{ks}: expected float32 ({self.out_features},), got "
+                                  f"{ws.dtype} {tuple(ws.shape)}")
+                return
+            dev = self.bias.device if self.bias is not None else (
+                self.weight.device if self.weight is not None else Wq.device)
+            self.Wq = Wq.detach().to(dev).clone()
+            self.w_scale = ws.detach().to(dev).clone()
+            self.weight = None
+            if self.bias is not None:
+                kb = prefix + "bias"
+                if kb in state_dict:
+                    with torch.no_grad():
+                        self.bias.copy_(state_dict[kb])
+                elif strict:
+                    missing_keys.append(kb)
+            if kw in state_dict:
+                unexpected_keys.append(kw)
+            return
+        if self.weight is None:
+            # a quantized layer loading an fp16 weight: back to the fp16 form
+            if kw in state_dict:
+                self.weight = torch.nn.Parameter(torch.empty(
+                    (self.out_features, self.in_features), dtype=torch.float16,
+                    device=self.Wq.device), requires_grad=False)
+                self.Wq = None
+                self.w_scale = None
+        super()._load_from_state_dict(state_dict, prefix, local_metadata, strict, missing_keys,
+                                      unexpected_keys, error_msgs)
+
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.dtype != torch.float16:
             raise TypeError(f"Int8Linear takes float16 inputs, got {x.dtype}")
@@ -113,7 +157,8 @@ def replace_linear_with_int8(module: torch.nn.Module,
                              _prefix: str = "") -> torch.nn.Module:
     """Replaces, in place, every float16 nn.Linear of ``module`` by an
     Int8Linear, except layers with fewer than ``min_in_features`` inputs and
-    layers whose qualified name, or any part of it, is in ``skip_modules``.
+    layers whose own name or qualified name (``block.q_proj``) is in
+    ``skip_modules``.
     Returns ``module``."""
     skip = set(skip_modules or ())
     for name, child in list(module.named_children()):

@@ -102,6 +102,13 @@ def test_int8linear_module_matches_oracle(lib):
     y2 = m(x)
     torch.cuda.synchronize()
     assert np.array_equal(y2.cpu().numpy().view(np.uint16), y.cpu().numpy().view(np.uint16))
+    # the prepared layer's state dict loads into a fresh layer as it is
+    m3 = lib.Int8Linear(K, N, bias=True, threshold=6.0, device="cuda")
+    m3.load_state_dict(m.state_dict())
+    y3 = m3(x)
+    torch.cuda.synchronize()
+    assert m3.quantized and m3.weight is None
+    assert np.array_equal(y3.cpu().numpy().view(np.uint16), y.cpu().numpy().view(np.uint16))
 
 
 def test_replace_linear_with_int8_runs(lib):

@@ -74,3 +74,27 @@ def test_suggest_threshold_from_stats():
     assert mm.suggest_threshold(stats=stats, max_fp16_fraction=0.01) == float("inf")
     with pytest.raises(ValueError):
         mm.suggest_threshold(stats={"K": 10, "n_outliers": {}}, candidates=(6.0,))
+
+
+def test_state_dict_of_a_prepared_layer_loads_without_requantizing():
+    # a prepared layer's state (fabricated here: preparing needs a GPU)
+    q = {"Wq": torch.arange(512 * 128, dtype=torch.int32).remainder(255).sub(127)
+               .to(torch.int8).reshape(512, 128),
+         "w_scale": torch.linspace(0.1, 1.0, 300),
+         "bias": torch.full((300,), 0.5, dtype=torch.float16)}
+    m = mm.Int8Linear(70, 300)
+    assert sorted(m.state_dict()) == ["bias", "weight"]
+    m.load_state_dict(q)
+    assert m.quantized and m.weight is None
+    assert torch.equal(m.Wq, q["Wq"]) and torch.equal(m.w_scale, q["w_scale"])
+    assert sorted(m.state_dict()) == ["Wq", "bias", "w_scale"]
+    m2 = mm.Int8Linear(70, 300)
+    m2.load_state_dict(m.state_dict())
+    assert m2.quantized and torch.equal(m2.Wq, m.Wq)
+    # an fp16 state turns a prepared layer back into the fp16 form
+    m2.load_state_dict(mm.Int8Linear(70, 300).state_dict())
+    assert not m2.quantized and m2.weight.shape == (300, 70)
+    # a prepared weight of the wrong shape is refused
+    bad = dict(q, Wq=torch.zeros((256, 128), dtype=torch.int8))
+    with pytest.raises(RuntimeError, match="Wq"):
+        mm.Int8Linear(70, 300).load_state_dict(bad)

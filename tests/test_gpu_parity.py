@@ -164,3 +164,22 @@ def test_output_overflow_gives_inf(lib):
     W[1] = -60.0
     Y, Y_ref = run_case(lib, X, W, 1000.0)
     assert np.isinf(Y_ref).all()
+
+
+@pytest.mark.parametrize("M,t", [(3, math.inf), (20, math.inf), (3, 6.0), (20, 6.0)])
+def test_maximum_k_at_the_int32_bound(lib, M, t):
+    # K = the largest accepted: every code is +-127, so |C| reaches
+    # 127^2 * K = 2147479576 (just below 2^31) with no outlier column, on
+    # both kernels (decode M <= 16, prefill with its K split); with t = 6
+    # three planted columns leave the int8 part
+    K, N = 133144, 64
+    print(f"case max K M={M} K={K} N={N} t={t}", flush=True)
+    X = np.ones((M, K), np.float16)
+    X[1::2] = np.float16(-1.0)
+    if t != math.inf:
+        X[:, [7, 70000, K - 1]] = np.float16(30.0)
+    W = np.full((N, K), 0.25, np.float16)
+    W[::3] = np.float16(-0.25)
+    Y, Y_ref = run_case(lib, X, W, t)
+    if t == math.inf:  # |C| = 127^2 K exactly (checked bit for bit by run_case): Y = fp16(K/4)
+        assert np.all(np.abs(Y_ref) == np.float16(0.25 * K))

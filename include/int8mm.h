@@ -31,6 +31,10 @@
  *   - No global mutable state: calls on different streams with different
  *     workspaces may run concurrently.  Two calls that share a workspace
  *     must be ordered (e.g. on one stream).
+ *   - A call can be captured in a HIP graph and replayed: it records only
+ *     kernel launches (counters and fills are cleared by kernels, never by
+ *     hipMemsetAsync), and every counter it relies on is cleared by an
+ *     earlier kernel of the same call.
  *   - X and Y are row-major.  The int8 operands and the fp16 outlier slices
  *     (the prepared weight Wq, and the stage outputs Xq, X_O, W_O) use the
  *     library's panel-tiled layout, built for gfx950's memory path: rows are

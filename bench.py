@@ -18,6 +18,12 @@ of 10 more calls against HBM bandwidth).  Prints one JSON line.
                by HBM (8 TB/s); traffic comes from the committed rocprofv3
                FETCH_SIZE / WRITE_SIZE counters when they match the current
                kernel sources, else null.
+* warm-up   -- W calls, continued until it has lasted at least 50 ms
+               (warmup_calls_run says how many ran): the clocks need that long
+               under load to settle, and value is the steady-state rate.
+* per_call  -- median and minimum of per-call times (HIP events around each
+               whole call, and the kernel's own stamps), from passes after
+               the timed region.
 * cpu_baseline -- the CPU oracle (oracle/, unchanged) timed on this host on
                the same workload (or a row sample of it for the largest
                ones), in the same unit.
@@ -38,6 +44,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "effective TOPS of decomposed int8 matmul; % int8 MFMA peak / % HBM BW"
+WARMUP_MIN_S = 0.05  # shortest warm-up: clocks settle within tens of milliseconds
 PEAK_INT8_TOPS = 5000.0    # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP16_TOPS = 2500.0    # MI355X dense fp16 MFMA, 2.5 PFLOP/s
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
@@ -225,7 +232,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="q_proj")
     ap.add_argument("--threshold", type=float, default=None)
     ap.add_argument("--rotate", type=int, default=None,
@@ -324,8 +331,16 @@ def main() -> int:
         if st != 0:
             raise mm.Int8mmError("int8_matmul_profiled", st)
 
-    for i in range(args.warmup):
-        step(i)
+    # W untimed warm-up calls, continued (untimed) until the warm-up has
+    # lasted WARMUP_MIN_S: the GPU's clocks need several milliseconds of
+    # sustained work to settle, and the rate reported is the steady one
+    w0 = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - w0 < WARMUP_MIN_S:
+        step(n_warm)
+        n_warm += 1
+        if n_warm >= args.warmup and n_warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # timed region: K plain calls
@@ -346,9 +361,23 @@ def main() -> int:
     torch.cuda.synchronize()
     kern_ms = [ev.elapsed_ms(a, b) for (a, b) in evs]
     kern_avg = float(np.mean(kern_ms))
+    # and once more with a HIP event pair around each whole call, for the
+    # per-call median and minimum (the events add gaps: not the timed value)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        ev.hip.hipEventRecord(evs[i][0], stream)
+        step(i)
+        ev.hip.hipEventRecord(evs[i][1], stream)
+    torch.cuda.synchronize()
+    call_ms = [ev.elapsed_ms(a, b) for (a, b) in evs]
     for a, b in evs:
         ev.destroy(a)
         ev.destroy(b)
+    per_call = {"call_ms_median": round(float(np.median(call_ms)), 5),
+                "call_ms_min": round(float(np.min(call_ms)), 5),
+                "kernel_ms_median": round(float(np.median(kern_ms)), 5),
+                "kernel_ms_min": round(float(np.min(kern_ms)), 5),
+                "timing": f"HIP events per call over {args.steps} calls after the timed region"}
     ev.destroy(p0)
     ev.destroy(p1)
     assert torch.isfinite(Y).all().item() or args.config == "tiny", "non-finite output"
@@ -393,6 +422,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls_run": n_warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -404,6 +434,7 @@ def main() -> int:
                    "weight_copies": n_copies, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "per_call": per_call,
         "prepare_weight_ms": round(prepare_ms, 4),
         "prepare_weight": prepare,
         "kernel_source_hash": src_hash,

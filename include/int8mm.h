@@ -24,6 +24,8 @@
  *     synchronises the host and enqueues all work on `stream` (0 = the null
  *     stream).
  *   - float16 data is passed as IEEE binary16 bit patterns (int8mm_half).
+ *     Every element pointer must be aligned to its element size (2 bytes
+ *     for float16, 4 for float and int32; INT8MM_EINVAL otherwise).
  *   - All argument checks run on the host before anything is enqueued; a
  *     failed check returns a negative status and enqueues nothing.
  *   - HIP launch failures return INT8MM_EHIP; the error text is available

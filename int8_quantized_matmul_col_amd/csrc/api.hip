@@ -80,6 +80,8 @@ int check_shape(int64_t M, int64_t K, int64_t N) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+// float16 / float / int32 data: naturally aligned elements
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 template <typename T>
 T* at(void* ws, size_t off) {
@@ -111,6 +113,10 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
   if (w_scale == nullptr) return INT8MM_EINVAL;
   // panel-tiled buffers take 16-byte loads and stores
   if (!aligned16(Wq) || !aligned16(out.Xq) || !aligned16(out.X_O) || !aligned16(out.W_O))
+    return INT8MM_EINVAL;
+  if (!aligned(X, 2) || !aligned(bias, 2) || !aligned(out.Y, 2) || !aligned(w_scale, 4) ||
+      !aligned(out.x_scale, 4) || !aligned(out.C, 4) || !aligned(out.n_outliers, 4) ||
+      !aligned(out.outlier_idx, 4))
     return INT8MM_EINVAL;
   const Layout L = make_layout(M, K, N);
   if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0 || ws_bytes < L.total)
@@ -213,7 +219,7 @@ INT8MM_API int int8_prepare_weight(const int8mm_half* W, int64_t N, int64_t K, i
   if (N < 0 || K < 0 || K > INT8MM_MAX_K || N > kMaxRows) return INT8MM_ESHAPE;
   if (N == 0) return INT8MM_OK;
   if (w_scale == nullptr || (K > 0 && (W == nullptr || Wq == nullptr))) return INT8MM_EINVAL;
-  if (!aligned16(Wq)) return INT8MM_EINVAL;
+  if (!aligned16(Wq) || !aligned(W, 2) || !aligned(w_scale, 4)) return INT8MM_EINVAL;
   hipError_t e = i8mm::launch_prepare_weight(W, (int)N, (int)K, (int)ld_of(K), Wq, w_scale, stream);
   if (e != hipSuccess) return hip_fail(e);
   return INT8MM_OK;
@@ -249,6 +255,7 @@ INT8MM_API int int8_column_absmax(const int8mm_half* X, int64_t M, int64_t K,
   if (st != INT8MM_OK) return st;
   if (K == 0) return INT8MM_OK;
   if (colmax == nullptr || (M > 0 && X == nullptr)) return INT8MM_EINVAL;
+  if (!aligned(X, 2) || !aligned(colmax, 2)) return INT8MM_EINVAL;
   hipError_t e;
   if (M == 0) {  // no rows: every column maximum is 0
     if ((e = i8mm::launch_zero_half(colmax, K, stream)) != hipSuccess) return hip_fail(e);

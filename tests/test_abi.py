@@ -132,6 +132,18 @@ def test_matmul_rejects_bad_arguments(lib):
     assert _mm(lib, Wq=FAKE + 8) == binding.INT8MM_EINVAL
 
 
+def test_element_pointers_must_be_aligned(lib):
+    # float16 pointers on odd addresses, float pointers off 4 bytes
+    assert _mm(lib, X=FAKE + 1) == binding.INT8MM_EINVAL
+    assert _mm(lib, Y=FAKE + 1) == binding.INT8MM_EINVAL
+    assert _mm(lib, s=FAKE + 2) == binding.INT8MM_EINVAL
+    assert _lin(lib, b=FAKE + 1) == binding.INT8MM_EINVAL
+    assert lib.int8_prepare_weight(FAKE + 1, 4, 8, FAKE, FAKE, None) == binding.INT8MM_EINVAL
+    assert lib.int8_prepare_weight(FAKE, 4, 8, FAKE, FAKE + 2, None) == binding.INT8MM_EINVAL
+    assert lib.int8_column_absmax(FAKE + 1, 4, 8, FAKE, FAKE_WS, 1 << 30, None) == binding.INT8MM_EINVAL
+    assert lib.int8_column_absmax(FAKE, 4, 8, FAKE + 1, FAKE_WS, 1 << 30, None) == binding.INT8MM_EINVAL
+
+
 def test_matmul_empty_is_a_noop(lib):
     # nothing to compute: returns OK without touching any pointer
     assert _mm(lib, M=0, X=FAKE, Y=FAKE) == binding.INT8MM_OK

@@ -228,6 +228,23 @@ def test_zero_bias_is_no_bias():
     assert np.array_equal(Y0, Y1)
 
 
+def test_dequantized_outlier_weight_exhaustive():
+    # W_O = the exact q * a_w / 127 rounded to fp32, then to fp16, for every
+    # code q and every positive normal fp16 scale a_w.  The exact quotient is
+    # formed in float64 (q*a_w has at most 19 significant bits, and p/127 is
+    # never closer than 2^-31 relative to an fp32 rounding tie, far beyond
+    # float64's 2^-53), so one rounding to fp32 here is the correct rounding.
+    a = np.arange(0x0400, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    q = np.arange(-127, 128, dtype=np.int8)
+    Wq = np.repeat(q[None, :], a.size, axis=0)  # [N = #scales][K = 255 codes]
+    O = np.arange(255)
+    X = np.zeros((1, 255), np.float16)
+    _, W_O = ref.outlier_slices_ref(X, Wq, a, O)  # [|O|][N]
+    exact = (q.astype(np.float64)[:, None] * a.astype(np.float64)[None, :]) / 127.0
+    want = exact.astype(np.float32).astype(np.float16)
+    assert np.array_equal(W_O.view(np.uint16), want.view(np.uint16))
+
+
 def test_round_to_binary_matches_hardware_casts():
     rng = np.random.default_rng(11)
     vals = rng.standard_normal(2000) * np.exp2(rng.integers(-20, 20, 2000))

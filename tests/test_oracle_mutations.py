@@ -17,7 +17,8 @@ import test_accuracy_study as study
 
 _orig = {n: getattr(ref, n) for n in ("quantize_rows_ref", "outlier_mask_ref",
                                       "quantize_activation_ref", "outlier_slices_ref",
-                                      "outlier_gemm_ref", "epilogue_ref", "int8_gemm_ref")}
+                                      "outlier_gemm_ref", "epilogue_ref", "int8_gemm_ref",
+                                      "prepare_weight_ref")}
 
 
 def _round_half_away(A16, scale):
@@ -99,6 +100,28 @@ def _bias_reversed_index(C, a_x, a_w, Y_O, bias=None):
     return _orig["epilogue_ref"](C, a_x, a_w, Y_O, rb)
 
 
+# (Forming W_O as fp16(fp32(Wq/127) * a_w) is not among the mistakes: the two
+# fp32 roundings can move the value by one fp32 ulp, but the exact quotient
+# q*a_w/127 is never within 2^-18 (relative) of an fp16 rounding tie, so the
+# fp16 result is the same for every code and scale.)
+
+
+def _outlier_columns_shifted(X16, Wq, a_w, O):
+    # the slices taken one feature to the right of the outlier columns
+    K = np.asarray(X16).shape[1]
+    return _orig["outlier_slices_ref"](X16, Wq, a_w, (np.asarray(O) + 1) % max(K, 1))
+
+
+def _weight_scale_per_tensor(W16):
+    W16 = np.asarray(W16, np.float16)
+    N, K = W16.shape
+    if K == 0:
+        return np.zeros((N, 0), np.int8), np.zeros(N, np.float32)
+    a = np.float32(np.abs(W16).max())
+    a_w = np.full(N, a, np.float32)
+    return _orig["quantize_rows_ref"](W16, a_w), a_w
+
+
 def _gemm_transposed_k(Xq, Wq, chunk=2048):
     # contracts against the reversed feature axis of W
     return _orig["int8_gemm_ref"](Xq, Wq[:, ::-1].copy(), chunk)
@@ -115,6 +138,8 @@ MUTATIONS = {
     "dequant_by_127_not_127sq": ("epilogue_ref", _epilogue_single_127),
     "outlier_term_sign": ("epilogue_ref", _epilogue_wrong_sign),
     "gemm_wrong_k_index": ("int8_gemm_ref", _gemm_transposed_k),
+    "outlier_columns_shifted": ("outlier_slices_ref", _outlier_columns_shifted),
+    "weight_scale_per_tensor": ("prepare_weight_ref", _weight_scale_per_tensor),
     "bias_dropped": ("epilogue_ref", _bias_dropped),
     "bias_wrong_sign": ("epilogue_ref", _bias_sign),
     "bias_wrong_index": ("epilogue_ref", _bias_reversed_index),
@@ -136,6 +161,7 @@ def _run_pins():
         ("strict", pins.test_strict_threshold_comparison, ()),
         ("bf_bias_4x8x4", pins.test_bruteforce_4x8x4_with_bias, ()),
         ("accuracy_claims", study.test_accuracy_claims_on_the_oracle, ()),
+        ("w_o_exhaustive", pins.test_dequantized_outlier_weight_exhaustive, ()),
     ] + [(f"bf_random_{s}", pins.test_bruteforce_random_small, (s,)) for s in range(6)] + [
         (f"bf_bias_random_{s}", pins.test_bruteforce_random_small_with_bias, (s,))
         for s in range(4)]

@@ -102,7 +102,7 @@ def _bias_reversed_index(C, a_x, a_w, Y_O, bias=None):
 
 # (Forming W_O as fp16(fp32(Wq/127) * a_w) is not among the mistakes: the two
 # fp32 roundings can move the value by one fp32 ulp, but the exact quotient
-# q*a_w/127 is never within 2^-18 (relative) of an fp16 rounding tie, so the
+# q*a_w/127 is never within about 2^-19 (relative) of an fp16 rounding tie, so the
 # fp16 result is the same for every code and scale.)
 
 

@@ -54,7 +54,7 @@ def check_y(Y: np.ndarray, Y_ref: np.ndarray, X16, Wq_r, s_r, n_out, what="Y", b
     fin = np.isfinite(yr)
     assert np.array_equal(np.isfinite(y), fin), f"{what}: non-finite pattern"
     assert np.array_equal(y[~fin], yr[~fin]), f"{what}: infinities"
-    d = np.abs(y - yr)[fin]
+    d = np.abs(y[fin] - yr[fin])
     assert np.all(d <= loose[fin]), f"{what}: max excess {np.max(d - loose[fin])}"
     bad = d > tight[fin]
     assert not bad.any(), f"{what}: {bad.sum()} elements beyond 1 ulp, worst {np.max(d - tight[fin])}"

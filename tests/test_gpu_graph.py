@@ -3,7 +3,8 @@ nothing and never synchronizes, so a call can be captured in a HIP graph and
 replayed.  Each case captures one call (prefill and decode shapes, with and
 without a bias), then replays it several times with new activations copied
 in eagerly between replays, and checks every replay bit for bit against an
-eager call on the same inputs."""
+eager call on the same inputs.  Calls on two streams with their own
+workspaces run concurrently and give the single-stream results."""
 
 import numpy as np
 import pytest
@@ -53,3 +54,27 @@ def test_graph_replay_matches_eager(lib, M, K, N, with_bias):
             Ye = lib.int8_linear(x, Wq, s, b, threshold=6.0)  # eager, own buffers
             torch.cuda.synchronize()
             assert torch.equal(got.view(torch.int16), Ye.view(torch.int16)), (rep, M)
+
+
+def test_concurrent_calls_on_two_streams(lib):
+    # no global mutable state: calls on two streams with their own workspaces
+    # overlap freely and each gives the eager single-stream result
+    import torch
+    print("case two streams", flush=True)
+    cases = []
+    for i, (M, K, N) in enumerate([(300, 2112, 520), (8, 2048, 1024)]):
+        W = workloads.make_w(N, K, 700 + i, 0.02)
+        Wq, s = lib.int8_prepare_weight(to_dev(W))
+        X = to_dev(workloads.make_x(M, K, 800 + i, 4, 8.0, 60.0, "uniform")[0])
+        ref_y = lib.int8_matmul(X, Wq, s, threshold=6.0)
+        cases.append((X, Wq, s, ref_y, lib.workspace_for(M, K, N, X.device),
+                      torch.empty((M, N), dtype=torch.float16, device="cuda")))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    for _ in range(5):
+        for (X, Wq, s, _, ws, Y), st in zip(cases, streams):
+            with torch.cuda.stream(st):
+                lib.int8_matmul(X, Wq, s, threshold=6.0, out=Y, workspace=ws)
+    torch.cuda.synchronize()
+    for X, Wq, s, ref_y, ws, Y in cases:
+        assert torch.equal(Y.view(torch.int16), ref_y.view(torch.int16))

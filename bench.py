@@ -21,6 +21,9 @@ of 10 more calls against HBM bandwidth).  Prints one JSON line.
 * warm-up   -- W calls, continued until it has lasted at least 50 ms
                (warmup_calls_run says how many ran): the clocks need that long
                under load to settle, and value is the steady-state rate.
+* other_entry_points -- the same workload through int8_linear (with a
+               bias) and int8_column_absmax, K calls each after the timed
+               region.
 * per_call  -- median and minimum of per-call times (HIP events around each
                whole call, and the kernel's own stamps), from passes after
                the timed region.
@@ -389,6 +392,47 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # the other entry points on the same workload, after the timed region:
+    # the layer forward with a bias (int8_linear) in rounds interleaved with
+    # int8_matmul (so that both see the same clock), and the column maxima
+    # (int8_column_absmax)
+    bias = (torch.arange(N, device=dev, dtype=torch.float32) % 7 - 3).to(torch.float16) / 8
+    lin, cmx = lib.int8_linear, lib.int8_column_absmax
+    cm = torch.empty((K,), dtype=torch.float16, device=dev)
+
+    def step_lin(i):
+        wp, sp = args_w[i % len(args_w)]
+        st = lin(xp, M, K, wp, sp, N, bias.data_ptr(), float(t), yp, ws_ptr, ws_bytes, stream)
+        if st != 0:
+            raise mm.Int8mmError("int8_linear", st)
+
+    def step_cmx(i):
+        st = cmx(xp, M, K, cm.data_ptr(), ws_ptr, ws_bytes, stream)
+        if st != 0:
+            raise mm.Int8mmError("int8_column_absmax", st)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    n_round = max(1, min(args.steps, 20))
+    mm_ms, lin_ms = [], []
+    for _ in range(4):
+        mm_ms.append(timed(step, n_round))
+        lin_ms.append(timed(step_lin, n_round))
+    colmax_ms = timed(step_cmx, args.steps)
+    others = {"int8_linear_ms": round(float(np.median(lin_ms)), 5),
+              "int8_matmul_ms_same_rounds": round(float(np.median(mm_ms)), 5),
+              "int8_column_absmax_ms": round(colmax_ms, 5),
+              "column_absmax_GB/s": round(M * K * 2 / (colmax_ms * 1e-3) / 1e9, 1),
+              "timing": (f"wall clock; int8_linear (with a bias) and int8_matmul in 4 interleaved "
+                         f"rounds of {n_round} calls (medians), int8_column_absmax over "
+                         f"{args.steps} calls; all after the timed region")}
+
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
     decode = M <= mm.INT8MM_DECODE_MAX_M
@@ -437,6 +481,7 @@ def main() -> int:
         "per_call": per_call,
         "prepare_weight_ms": round(prepare_ms, 4),
         "prepare_weight": prepare,
+        "other_entry_points": others,
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(out), flush=True)

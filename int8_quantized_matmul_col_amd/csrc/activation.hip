@@ -146,11 +146,12 @@ __global__ __launch_bounds__(256) void k_colmask(const uint16_t* __restrict__ X,
 // Exclusive prefix counts of the mask words into s_pre[], mask words into
 // s_bits[] (from mask_bits; or already there when mask_bits is null); returns
 // |O|.  Called by all 256 threads of the block.
+template <int T = 256>
 __device__ int load_mask_prefix(const uint32_t* __restrict__ mask_bits, int nw,
                                 uint32_t* s_bits, int* s_pre) {
-  __shared__ int s_wsum[4];
+  __shared__ int s_wsum[T / 64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int per = (nw + 255) / 256;
+  const int per = (nw + T - 1) / T;
   const int w0 = min(nw, t * per), w1 = min(nw, w0 + per);
   int local = 0;
   for (int w = w0; w < w1; ++w) {
@@ -173,7 +174,7 @@ __device__ int load_mask_prefix(const uint32_t* __restrict__ mask_bits, int nw,
   __syncthreads();
   int before = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < T / 64; ++w) {
     before += (w < wave) ? s_wsum[w] : 0;
     total += s_wsum[w];
   }
@@ -597,14 +598,14 @@ __global__ __launch_bounds__(256) void k_quant_rows(
 // mask words, |O| and the optional mask bytes and O list.  CPT = 8-column
 // chunks per thread (ldk <= 256 * 8 * CPT); rows are 16-byte aligned and
 // K % 8 == 0.  Dynamic LDS: 2*nw words.
-template <int CPT>
-__global__ __launch_bounds__(256) void k_activation_small(
+template <int CPT, int T>
+__global__ __launch_bounds__(T) void k_activation_small(
     const uint16_t* __restrict__ X, int M, int K, int ldk, float threshold,
     uint8_t* __restrict__ mask8, uint32_t* __restrict__ mask_bits, int32_t* __restrict__ n_out,
     int32_t* __restrict__ out_idx, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
     uint16_t* __restrict__ XO) {
   extern __shared__ uint32_t s_dyn[];
-  __shared__ uint32_t s_red[4];
+  __shared__ uint32_t s_red[T / 64];
   const int nw = ldk / 32, nch = ldk / 8, nck = K >> 3;
   uint32_t* s_bits = s_dyn;
   int* s_pre = reinterpret_cast<int*>(s_dyn + nw);
@@ -617,7 +618,7 @@ __global__ __launch_bounds__(256) void k_activation_small(
   uint4 hv[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
-    const int c = t + u * 256;
+    const int c = t + u * T;
     uint32_t mx[4] = {0u, 0u, 0u, 0u};  // |x| bits, two columns per word
     hv[u] = uint4{0u, 0u, 0u, 0u};
     if (c < nck) {
@@ -649,16 +650,16 @@ __global__ __launch_bounds__(256) void k_activation_small(
     }
   }
   __syncthreads();
-  const int total = load_mask_prefix(nullptr, nw, s_bits, s_pre);
+  const int total = load_mask_prefix<T>(nullptr, nw, s_bits, s_pre);
   const int opad = (total + 63) & ~63;
 
   if (m == 0) {
-    for (int w = t; w < nw; w += 256) mask_bits[w] = s_bits[w];
+    for (int w = t; w < nw; w += T) mask_bits[w] = s_bits[w];
     if (mask8 != nullptr)
-      for (int k = t; k < K; k += 256) mask8[k] = (uint8_t)((s_bits[k >> 5] >> (k & 31)) & 1u);
+      for (int k = t; k < K; k += T) mask8[k] = (uint8_t)((s_bits[k >> 5] >> (k & 31)) & 1u);
     if (t == 0 && n_out != nullptr) *n_out = total;
     if (out_idx != nullptr) {
-      for (int w = t; w < nw; w += 256) {
+      for (int w = t; w < nw; w += T) {
         uint32_t b = s_bits[w];
         int slot = s_pre[w];
         while (b) {
@@ -673,25 +674,27 @@ __global__ __launch_bounds__(256) void k_activation_small(
   uint32_t mx2 = 0;
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
-    const int c = t + u * 256;
+    const int c = t + u * T;
     const uint32_t ob = c < nch ? (uint32_t)s_ob[c] : 0u;
     mx2 = pk_max_u16(mx2, chunk_absmax2(hv[u], ob));
   }
   uint32_t mx = wave_max(max(mx2 & 0xffffu, mx2 >> 16));
   if (lane == 0) s_red[wave] = mx;
   __syncthreads();
-  mx = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+  mx = 0;
+#pragma unroll
+  for (int w = 0; w < T / 64; ++w) mx = max(mx, s_red[w]);
   const float a = h2f((uint16_t)mx);
   const float r = a == 0.0f ? 0.0f : 127.0f / a;
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
-    const int c = t + u * 256;
+    const int c = t + u * T;
     if (c < nch)
       *reinterpret_cast<uint2*>(Xq + tiled_offset(m, (size_t)c * 8, ldk)) =
           code_chunk(hv[u], m, s_bits[c >> 2], (c & 3) * 8, s_pre[c >> 2], r, a, ldk, XO);
   }
   if (XO != nullptr)
-    for (int j = total + t; j < opad; j += 256)
+    for (int j = total + t; j < opad; j += T)
       XO[tiled_offset(m, (size_t)j * 2, (size_t)ldk * 2) / 2] = 0;
   if (t == 0) x_scale[m] = a;
 }
@@ -780,7 +783,7 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
 
 bool activation_small_ok(const uint16_t* X, int M, int K, int ldk) {
   return M >= 1 && M <= 16 && (K % 8) == 0 && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
-         ldk / 8 <= 256 * 8;
+         ldk / 8 <= 1024 * 2;
 }
 
 hipError_t launch_activation_small(const uint16_t* X, int M, int K, int ldk, float threshold,
@@ -789,12 +792,12 @@ hipError_t launch_activation_small(const uint16_t* X, int M, int K, int ldk, flo
                                    hipStream_t s) {
   const int nch = ldk / 8;
   const size_t lds = (size_t)2 * (ldk / 32) * sizeof(uint32_t);
-  const int cpt = (nch + 255) / 256;
-#define AS(C) hipLaunchKernelGGL((k_activation_small<C>), dim3(M), dim3(256), lds, s, X, M, K, ldk, threshold, mask8, mask_bits, n_out, out_idx, Xq, x_scale, XO)
-  if (cpt <= 1) AS(1);
-  else if (cpt <= 2) AS(2);
-  else if (cpt <= 4) AS(4);
-  else AS(8);
+  // one thread per 8-column chunk where it fits: all the loads of a row in
+  // one round (1024 threads up to 8192 columns, two chunks each beyond)
+#define AS(C, T) hipLaunchKernelGGL((k_activation_small<C, T>), dim3(M), dim3(T), lds, s, X, M, K, ldk, threshold, mask8, mask_bits, n_out, out_idx, Xq, x_scale, XO)
+  if (nch <= 256) AS(1, 256);
+  else if (nch <= 1024) AS(1, 1024);
+  else AS(2, 1024);
 #undef AS
   return hipGetLastError();
 }

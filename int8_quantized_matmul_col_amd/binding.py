@@ -112,6 +112,17 @@ def _require(t, dtype, name: str, device=None) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_out(t, shape, dtype, name: str, device=None) -> None:
+    """A caller-supplied output buffer must have exactly the shape the
+    kernels write (they write every element of it, and nothing beyond)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _require(t, dtype, name, device)
+
+
 def int8_weight_ld(K: int) -> int:
     """Row stride of the prepared weight and of the [.][ldk] stage buffers."""
     return int(load().int8_weight_ld(int(K)))
@@ -166,6 +177,8 @@ def int8_prepare_weight(W, out: Optional[Tuple] = None):
         ws = torch.empty((N,), dtype=torch.float32, device=W.device)
     else:
         Wq, ws = out
+        _check_out(Wq, (padded_rows(N), ldk), torch.int8, "out[0] (Wq)", W.device)
+        _check_out(ws, (N,), torch.float32, "out[1] (w_scale)", W.device)
     st = lib.int8_prepare_weight(_ptr(W), N, K, _ptr(Wq), _ptr(ws), _stream(W.device))
     _check("int8_prepare_weight", st)
     return Wq, ws
@@ -197,7 +210,7 @@ def int8_matmul(X, Wq, w_scale, threshold: float = DEFAULT_THRESHOLD, out=None, 
                          f"w_scale {tuple(w_scale.shape)}")
     Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
     if out is not None:
-        _require(Y, torch.float16, "out", dev)
+        _check_out(Y, (M, N), torch.float16, "out", dev)
     ws = workspace if workspace is not None else workspace_for(M, K, N, dev)
     st = lib.int8_matmul(_ptr(X), M, K, _ptr(Wq), _ptr(w_scale), N, float(threshold), _ptr(Y),
                          _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
@@ -227,7 +240,7 @@ def int8_linear(X, Wq, w_scale, bias=None, threshold: float = DEFAULT_THRESHOLD,
             raise ValueError(f"bias has {bias.numel()} entries, expected {N}")
     Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
     if out is not None:
-        _require(Y, torch.float16, "out", dev)
+        _check_out(Y, (M, N), torch.float16, "out", dev)
     ws = workspace if workspace is not None else workspace_for(M, K, N, dev)
     st = lib.int8_linear(_ptr(X), M, K, _ptr(Wq), _ptr(w_scale), N, _ptr(bias), float(threshold),
                          _ptr(Y), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
@@ -247,9 +260,7 @@ def int8_column_absmax(X, out=None, workspace=None):
     M, K = X.shape
     cm = out if out is not None else torch.empty((K,), dtype=torch.float16, device=dev)
     if out is not None:
-        _require(cm, torch.float16, "out", dev)
-        if cm.numel() != K:
-            raise ValueError(f"out has {cm.numel()} entries, expected {K}")
+        _check_out(cm, (K,), torch.float16, "out", dev)
     ws = workspace if workspace is not None else workspace_for(M, K, 0, dev)
     st = lib.int8_column_absmax(_ptr(X), M, K, _ptr(cm), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(dev))
@@ -261,9 +272,11 @@ def int8_matmul_profiled(X, Wq, w_scale, threshold: float, out, workspace, ev_st
                          ev_stop: int):
     """int8_matmul with raw hipEvent_t handles recorded around the matmul
     kernel (for timing that kernel alone).  All tensors preallocated."""
+    import torch
     lib = load()
     M, K = X.shape
     N = w_scale.numel()
+    _check_out(out, (M, N), torch.float16, "out", X.device)
     st = lib.int8_matmul_profiled(_ptr(X), M, K, _ptr(Wq), _ptr(w_scale), N, float(threshold),
                                   _ptr(out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(),

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_colmask(const uint16_t* __restrict__ X,
 
 // Exclusive prefix counts of the mask words into s_pre[], mask words into
 // s_bits[] (from mask_bits; or already there when mask_bits is null); returns
-// |O|.  Called by all 256 threads of the block.
+// |O|.  Called by all T threads of the block.
 template <int T = 256>
 __device__ int load_mask_prefix(const uint32_t* __restrict__ mask_bits, int nw,
                                 uint32_t* s_bits, int* s_pre) {
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(
 // shared through L2) to form the column absmax and the mask itself, then
 // quantizes row m, which it kept in registers.  Workgroup 0 also writes the
 // mask words, |O| and the optional mask bytes and O list.  CPT = 8-column
-// chunks per thread (ldk <= 256 * 8 * CPT); rows are 16-byte aligned and
+// chunks per thread (ldk <= T * 8 * CPT); rows are 16-byte aligned and
 // K % 8 == 0.  Dynamic LDS: 2*nw words.
 template <int CPT, int T>
 __global__ __launch_bounds__(T) void k_activation_small(

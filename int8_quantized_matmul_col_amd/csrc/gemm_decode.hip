@@ -84,9 +84,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   // of a group are 1 KiB contiguous per step
   const int8_t* xrow = Xq + tiled_offset(ml, kq, ldk);
   const bool xvalid = ml < M;
+  // The grid covers ceil(groups / G) * G groups of 16 rows, which can run past
+  // the prepared weight's padded rows when G does not divide the group count:
+  // such groups read the last padded row instead (their results are never
+  // stored, n >= N), so every load stays inside the weight.
+  const int row_cap = (int)padded_rows(N) - 1;
   const int8_t* wrow[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) wrow[g] = Wq + tiled_offset(n_base + g * 16 + ml, kq, ldk);
+  for (int g = 0; g < G; ++g)
+    wrow[g] = Wq + tiled_offset(min(n_base + g * 16 + ml, row_cap), kq, ldk);
 
   v4i acc[G];
   v4f acco[G];

@@ -1,33 +1,37 @@
 // Prefill GEMM of the decomposed int8 matmul on gfx950 matrix cores.
 //
-//   Y[m,n] = fp16( fp32(C[m,n]) * a_x[m]*a_w[n]/127^2 + sum_j X_O[m,j] W_O[n,j] )
+//   Y[m,n] = fp16( fp32(C[m,n]) * a_x[m]*a_w[n]/127^2 + b[n] + sum_j X_O[m,j] W_O[n,j] )
 //   C[m,n] = sum_k Xq[m,k] Wq[n,k]                         (int32, exact)
 //
 // ("LLM.int8() notes", section 2.3: the INT8 term plus the FP16 outlier term;
 // "PyTorch 2.9 supports LLM.int8()", section 3: results merged at the end.)
 //
-// One workgroup = 256x256 output tile, 8 waves, two per SIMD, in a 2x4
-// arrangement: each wave owns a 128x64 block held as 4x2
-// v_mfma_i32_32x32x32_i8 accumulators (128 AGPRs).  Two waves per SIMD let
-// one wave's memory and LDS instructions, which hold up the issuing wave,
-// overlap the other wave's MFMAs.  Operands are panel-tiled in memory
-// (tile_layout.h), so one 64-byte K step of a 256-row panel is 16 KiB
-// contiguous: each wave load instruction reads 1 KiB of whole cache lines.
-// Loads go to registers (three rotating one-step buffers, so a load has two
-// steps to land) and from there to LDS with swizzled ds_write_b128.  Five LDS
-// stages, each written three steps before it is computed: the one computed,
-// the next one (its first fragments are read before the current step ends),
-// the one written last step, the one being written, and one more, so that a
-// workgroup barrier is needed only after every second step; after the loop
-// the last two int8 stages are free for the epilogue.
+// One workgroup = 256x256 output tile, 4 waves, one per SIMD, each owning a
+// 128x128 block held as 4x4 v_mfma_i32_32x32x32_i8 accumulators (all 256
+// AGPRs).  Per 32-byte K sub-step a wave reads 4 + 4 fragments from LDS for
+// 16 MFMAs.  Operands are panel-tiled in memory (tile_layout.h): one 64-byte K
+// step of a 256-row panel is 16 KiB contiguous.
+//
+// Loads go straight from L2 into LDS (buffer_load_dwordx4 ... lds): each load
+// instruction fills 1 KiB of a stage, its lanes reading the 16-byte chunks
+// that the XOR swizzle of the fragment reads puts there.  Four stages of
+// 32 KiB (A block, then B block) form a ring; step kt+4's loads are issued
+// while step kt computes, and one workgroup barrier per step both publishes
+// the next stage and frees the one just consumed (see step()).  The loads are
+// branch-free: every buffer resource ends where its operand's valid steps
+// end, so the loads of steps past the last one fall outside it and fetch
+// nothing, and every step waits for the same load count.  (Conditional loads
+// measured ~20% slower: the scalar branches around them stall the issuing
+// wave while its MFMAs drain.)
 //
 // The outlier slice (|O| rounded up to 32 fp16 columns: 64 bytes per row per
-// step, the same byte shape as an int8 step) is appended to the same
-// pipeline as extra steps on v_mfma_f32_32x32x16_f16.  With at most three
-// such steps their operands are prefetched by the int8 loop and the fp16
-// products are added in the epilogue; with more, the int32 accumulators are
-// rescaled to fp32 and a loop of its own runs the fp16 steps (out of line).
-// |O| is read on the device: no host synchronisation.
+// step, the same byte shape as an int8 step) follows the int8 steps in the
+// same pipeline.  With at most three such steps they are only loaded by the
+// int8 loop, and the epilogue multiplies them from LDS per 32-row group
+// (v_mfma_f32_32x32x16_f16) onto fp32(C)*s + b; with more, the tile takes a
+// path of its own that rescales the int32 accumulators to fp32 in place and
+// continues the pipeline over the fp16 steps.  |O| is read on the device: no
+// host synchronisation.
 //
 // With few tiles (at most half as many as CUs) each tile is computed by two
 // workgroups that split K and exchange int32 partials (see k_gemm_prefill).
@@ -47,122 +51,104 @@ namespace {
 
 constexpr int BM = kPanelRows;  // 256
 constexpr int BN = kPanelRows;
-constexpr int NW = 8;           // waves per workgroup
+constexpr int NW = 4;           // waves per workgroup, one per SIMD
 constexpr int NT = 64 * NW;
-constexpr int NBUF = 5;  // LDS stages of 256 rows x 64 bytes per operand (160 KiB)
-constexpr int WM = 128;  // wave block rows (4 MFMA tiles)
-constexpr int WN = 64;   // wave block columns (2 MFMA tiles)
-constexpr int TI = WM / 32;
-constexpr int TJ = WN / 32;
+constexpr int NS = 4;                          // LDS stages
+constexpr int kStage = 2 * kTileBytes;         // A block then B block: 32 KiB
+constexpr int kScaleOff = NS * kStage;         // s_x[256], s_w[256], s_b[256], flag
+constexpr int kLds = kScaleOff + 3 * 1024 + 16;
+constexpr int WM = 128, WN = 128;              // wave block
+constexpr int TI = WM / 32, TJ = WN / 32;
+constexpr int kRsrcWord3 = 0x00020000;         // raw byte buffer
 
-struct Smem {
-  v4i a[NBUF][BM * 4];
-  v4i b[NBUF][BN * 4];
-};
-
-// LDS slot of 16-byte chunk `ch` (0..3) of tile row `row`.  gfx950 LDS serves
-// a 16-byte read in groups of 16 lanes (64 banks, 256 B/clk): 16 consecutive
-// rows then hit 16 distinct slots when the chunk is XORed with bits 2..3 of
-// the row.
-__device__ __forceinline__ int swz(int row, int ch) { return row * 4 + (ch ^ ((row >> 2) & 3)); }
-
-// Source of pipeline step s: int8 steps first, then fp16 outlier steps.
-struct Src {
-  const char* A;  // panel-tiled; the tile's panel already applied
-  const char* B;
-  const char* AO;
-  const char* BO;
-  int nk8;  // number of int8 steps
-};
-
-// One step's loads of one wave, in registers: 2 quads per operand.
-struct Stage4 {
-  v4i v[4];  // n = 2*i + operand
-};
-
-// Per-lane constants of the load path.  Load instruction n of wave w reads
-// the 1 KiB slice (n/2)*NW + w of the step block of operand n%2 (lane l: 16
-// bytes at +16l), i.e. LDS slot q = slice*64 + l, which it writes to the
-// swizzled position swz(q / 4, q % 4).
-struct LoadMap {
-  uint32_t goff[2];  // byte offset in the step block, per slice index i
-  int lidx[2];       // v4i index in an LDS stage
-};
-
-__device__ __forceinline__ LoadMap load_map(int wave, int lane) {
-  LoadMap mp;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = (i * NW + wave) * 64 + lane;
-    mp.goff[i] = (uint32_t)q * 16;
-    mp.lidx[i] = swz(q >> 2, q & 3);
-  }
-  return mp;
+// s_waitcnt immediate: vmcnt <= vm, lgkmcnt <= lgkm, expcnt not waited on
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
-// Block addresses of step s (clamped to the last step by the caller).
-__device__ __forceinline__ void step_src(const Src& src, int s, const char*& a, const char*& b) {
-  if (s < src.nk8) {
-    a = src.A + (size_t)s * kTileBytes;
-    b = src.B + (size_t)s * kTileBytes;
-  } else {
-    a = src.AO + (size_t)(s - src.nk8) * kTileBytes;
-    b = src.BO + (size_t)(s - src.nk8) * kTileBytes;
-  }
-}
-
-// Load instruction n (0..3) of a step into r.
-__device__ __forceinline__ void gload1(Stage4& r, const char* a, const char* b, int n,
-                                       const LoadMap& mp) {
-  const int i = n >> 1;
-  r.v[n] = *reinterpret_cast<const v4i*>(((n & 1) ? b : a) + mp.goff[i]);
-}
-
-__device__ __forceinline__ void gload_all(Stage4& r, const Src& src, int s, const LoadMap& mp) {
-  const char* a;
-  const char* b;
-  step_src(src, s, a, b);
-#pragma unroll
-  for (int n = 0; n < 4; ++n) gload1(r, a, b, n, mp);
-}
-
-// LDS write n (0..3) of a step's registers into stage buf.
-__device__ __forceinline__ void lwrite1(Smem& sm, int buf, const Stage4& r, int n,
-                                       const LoadMap& mp) {
-  const int i = n >> 1;
-  if (n & 1)
-    sm.b[buf][mp.lidx[i]] = r.v[n];
-  else
-    sm.a[buf][mp.lidx[i]] = r.v[n];
-}
-
-__device__ __forceinline__ void lwrite_all(Smem& sm, int buf, const Stage4& r, const LoadMap& mp) {
-#pragma unroll
-  for (int n = 0; n < 4; ++n) lwrite1(sm, buf, r, n, mp);
-}
-
-// MFMA operand fragments of one 32-byte K sub-step for the wave's 4x2 tiles.
 struct Frag {
   v4i a[TI];
   v4i b[TJ];
 };
 
-__device__ __forceinline__ void fload(Frag& f, const Smem& sm, int buf, int kk, int wm0, int wn0,
-                                      int lane) {
-  const int ch = kk * 2 + (lane >> 5);
+// Per-tile pipeline state, all wave-uniform except the per-lane offsets.
+struct Pipe {
+  __amdgpu_buffer_rsrc_t A;   // int8 step blocks (step s at s*16 KiB)
+  __amdgpu_buffer_rsrc_t B;
+  __amdgpu_buffer_rsrc_t AO;  // fp16 outlier step blocks
+  __amdgpu_buffer_rsrc_t BO;
+  int nk8;                    // int8 steps; steps nk8 .. last are outlier steps
+  int last;                   // last pipeline step
+  uint32_t goff;              // lane's byte offset in a step block for load 0
+  uint32_t ldsw;              // wave's byte offset in an operand's stage block
+  uint32_t ra[2];             // fragment read offsets in a stage, sub-step kk, A
+  uint32_t rb[2];             // ... B (includes the 16 KiB of the A block)
+};
+
+__device__ __forceinline__ void make_pipe(Pipe& p, const int8_t* Xq, const int8_t* Wq,
+                                          const uint16_t* XO, const uint16_t* WO, int tm, int tn,
+                                          int nk8, int k0, int n8, int n16, int wave, int lane) {
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  // each resource spans exactly the steps this workgroup consumes
+  p.A = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)Xq + ((size_t)tm * nk8 + k0) * kTileBytes), 0, n8 * kTileBytes,
+      kRsrcWord3);
+  p.B = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)Wq + ((size_t)tn * nk8 + k0) * kTileBytes), 0, n8 * kTileBytes,
+      kRsrcWord3);
+  // fp16 rows are 2*ldk bytes: panel t starts at t * 2*nk8 blocks
+  p.AO = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)XO + (size_t)tm * (2 * nk8) * kTileBytes), 0, n16 * kTileBytes,
+      kRsrcWord3);
+  p.BO = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const char*)WO + (size_t)tn * (2 * nk8) * kTileBytes), 0, n16 * kTileBytes,
+      kRsrcWord3);
+  p.nk8 = n8;
+  p.last = n8 + n16 - 1;
+  // load q of wave w fills LDS slots [(4q+w)*64, +64) of the operand block;
+  // lane l fills slot s = base + l: row s/4, stored chunk s%4, which holds
+  // logical chunk (s%4) ^ ((row/4)%4) (the swizzle of the fragment reads)
+  const int c = (lane & 3) ^ ((lane >> 4) & 3);
+  p.goff = (uint32_t)(wave * 1024 + (lane >> 2) * 64 + c * 16);
+  p.ldsw = (uint32_t)(wave * 1024);
+  // fragment read of tile row r, chunk ch: slot r*4 + (ch ^ ((r/4)%4)); 16
+  // consecutive rows hit 16 distinct slots of the 64 banks
+  const int r = lane & 31, sw = (r >> 2) & 3;
 #pragma unroll
-  for (int i = 0; i < TI; ++i) f.a[i] = sm.a[buf][swz(wm0 + i * 32 + (lane & 31), ch)];
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) f.b[j] = sm.b[buf][swz(wn0 + j * 32 + (lane & 31), ch)];
+  for (int kk = 0; kk < 2; ++kk) {
+    const int ch = (kk * 2 + (lane >> 5)) ^ sw;
+    p.ra[kk] = (uint32_t)((wm0 + r) * 64 + ch * 16);
+    p.rb[kk] = (uint32_t)(kTileBytes + (wn0 + r) * 64 + ch * 16);
+  }
 }
 
-__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+// Buffer resource and byte offset of operand b of pipeline step s (past the
+// last step: outside the outlier resource, so the load fetches nothing).
+struct Blk {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t off;
+};
+__device__ __forceinline__ Blk blk(const Pipe& p, int s, bool b) {
+  if (s < p.nk8) return Blk{b ? p.B : p.A, (uint32_t)s * kTileBytes};
+  return Blk{b ? p.BO : p.AO, (uint32_t)(s - p.nk8) * kTileBytes};
+}
 
-// One MFMA on fragment pair (w, x): the W fragment first.
+// Load q (0..3) of operand b of step s into stage s%NS.
+__device__ __forceinline__ void gload(char* lds, const Pipe& p, const Blk& src, int s, bool b,
+                                      int q) {
+  char* dst = lds + (s & (NS - 1)) * kStage + (b ? kTileBytes : 0) + q * 4096 + p.ldsw;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (__attribute__((address_space(3))) void*)dst,
+                                           16, p.goff, src.off + q * 4096, 0, 0);
+}
+
+__device__ __forceinline__ v4i lread(const char* lds, uint32_t off) {
+  return *reinterpret_cast<const v4i*>(lds + off);
+}
+
 template <bool F16>
 __device__ __forceinline__ void mma1(v16i& acc, const v4i& w, const v4i& x) {
   if constexpr (F16) {
-    // acc holds fp32 bit patterns here (reinterpreted in place)
+    // acc holds fp32 bit patterns here (rescaled in place)
     acc = __builtin_bit_cast(
         v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, w),
                                                      __builtin_bit_cast(v8h, x),
@@ -172,117 +158,100 @@ __device__ __forceinline__ void mma1(v16i& acc, const v4i& w, const v4i& x) {
   }
 }
 
+// Fragment read n (0..7) of sub-step kk in the order the MFMAs need them:
+// b0 a0 b1 b2 b3 a1 a2 a3 (MFMA t uses a[t/4], b[t%4]).
+__device__ __forceinline__ void fread1(Frag& f, const char* lds, uint32_t sbase, const Pipe& p,
+                                       int kk, int n) {
+  constexpr int kind[8] = {1, 0, 1, 1, 1, 0, 0, 0};
+  constexpr int idx[8] = {0, 0, 1, 2, 3, 1, 2, 3};
+  if (kind[n])
+    f.b[idx[n]] = lread(lds, sbase + p.rb[kk] + idx[n] * 2048);
+  else
+    f.a[idx[n]] = lread(lds, sbase + p.ra[kk] + idx[n] * 2048);
+}
+
 // One pipeline step kt, in a fixed instruction order (scheduling barriers
-// keep the compiler from regrouping it): 8 groups of 2 MFMAs (tiles (i, 0)
-// and (i, 1)), groups 0-3 on the sub-step-0 fragments f0 (i = group),
-// groups 4-7 on sub-step 1.  Fragment reads: sub-step 1 of this step into f1
-// during groups 0-2 (B fragments first), sub-step 0 of the next step into f0
-// during groups 4-6 (f0 is free after group 3).  Groups 0-3 also issue one
-// load each (step kt+5 into rl) and one LDS write each (step kt+3 from rw,
-// loaded during step kt-2).  The barrier comes after every second step
-// (sync: odd kt, and the last step of a run): a stage written in step j is
-// first read in step j+2, and one of steps j, j+1 ends with a barrier; the
-// stage written in step j last held step j-2, read in steps j-3 and j-2, and
-// one of steps j-2, j-1 ended with a barrier.  Branch-free otherwise: loads
-// past the last step are clamped to it (in bounds, written to stages of
-// steps past the last, which are not read again).
+// keep the compiler from regrouping it):
+//   phase 1: 16 MFMAs on f0 (sub-step 0 of kt); after each of the first 8 a
+//            fragment read of f1 (sub-step 1 of kt, stage kt%4); after MFMAs
+//            9, 11, 13, 15 a B load of step kt+3 into stage (kt+3)%4.
+//   wait + barrier: this wave's loads of step kt+1 have landed (the 16 loads
+//            of steps kt+2, kt+3 may still be in flight) and its fragment
+//            reads are done; after the barrier every wave's are, so stage
+//            (kt+1)%4 is complete and stage kt%4 is free.
+//   phase 2: 16 MFMAs on f1; reads of f0 (sub-step 0 of kt+1, stage
+//            (kt+1)%4); A loads of step kt+4 into stage kt%4.
+// Loads complete in issue order, so the loads of step j are the A half (phase
+// 2 of step j-4) then the B half (phase 1 of step j-3), and at the barrier of
+// step kt exactly 16 loads (steps kt+2, kt+3) were issued after step kt+1's.
 template <bool F16>
-__device__ __forceinline__ void step(Smem& sm, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
-                                     Stage4& rl, const Stage4& rw, const Src& src, int kt,
-                                     int last, int wm0, int wn0, const LoadMap& mp, int lane,
-                                     bool sync) {
-  const int cur = kt % NBUF, nxt = (kt + 1) % NBUF, wst = (kt + 3) % NBUF;
-  const char* ga;
-  const char* gb;
-  step_src(src, min(kt + 5, last), ga, gb);
-  const int r = lane & 31;
-  const int ch1 = 2 + (lane >> 5);  // sub-step 1 chunk
-  const int ch0 = (lane >> 5);      // sub-step 0 chunk
-  // fragment reads per group (6 per sub-step): b0 b1 | a0 a1 | a2 a3 | -
+__device__ __forceinline__ void step(char* lds, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
+                                     const Pipe& p, int kt) {
+  const uint32_t cur = (uint32_t)(kt & (NS - 1)) * kStage;
+  const uint32_t nxt = (uint32_t)((kt + 1) & (NS - 1)) * kStage;
+  const int sb = kt + NS - 1, sa = kt + NS;
+  const Blk gsb = blk(p, sb, true);
+  const Blk gsa = blk(p, sa, false);
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int i = g & 3;
-    Frag& fm = g < 4 ? f0 : f1;  // operands of this group's MFMAs
-    Frag& fr = g < 4 ? f1 : f0;  // fragments read in this group
-    const int rbuf = g < 4 ? cur : nxt;
-    const int rch = g < 4 ? ch1 : ch0;
-    const int gg = g & 3;
-    mma1<F16>(acc[i][0], fm.b[0], fm.a[i]);
+  for (int t = 0; t < 16; ++t) {
+    mma1<F16>(acc[t >> 2][t & 3], f0.b[t & 3], f0.a[t >> 2]);
     __builtin_amdgcn_sched_barrier(0);
-    if (gg == 0) {
-      fr.b[0] = sm.b[rbuf][swz(wn0 + r, rch)];
-      fr.b[1] = sm.b[rbuf][swz(wn0 + 32 + r, rch)];
-    } else if (gg < 3) {
-      const int i0 = (gg - 1) * 2;
-      fr.a[i0] = sm.a[rbuf][swz(wm0 + i0 * 32 + r, rch)];
-      fr.a[i0 + 1] = sm.a[rbuf][swz(wm0 + (i0 + 1) * 32 + r, rch)];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mma1<F16>(acc[i][1], fm.b[1], fm.a[i]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (g < 4) {
-      gload1(rl, ga, gb, g, mp);
-      lwrite1(sm, wst, rw, g, mp);
+    if (t < 8) {
+      fread1(f1, lds, cur, p, 1, t);
+      __builtin_amdgcn_sched_barrier(0);
+    } else if (t & 1) {
+      gload(lds, p, gsb, sb, true, (t - 8) >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // LDS operations complete in order: lgkmcnt(2) leaves only the last two
-  // fragment reads (needed from group 2 of the next step on) in flight, so
-  // this wave's stage writes have landed before the barrier
-  if (sync) {
-    __builtin_amdgcn_s_waitcnt(0xc27f);
-    __builtin_amdgcn_s_barrier();
-  }
-}
-
-// Steps kt of [k0, k1) in order; the register buffers rotate with kt mod 3
-// (step kt loads step kt+5 into buf[(kt+1)%3] and writes step kt+3 from
-// buf[(kt+2)%3]).  Unrolled by three so that the roles are static.
-template <bool F16>
-__device__ __forceinline__ void run_steps(Smem& sm, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
-                                          Stage4& b0, Stage4& b1, Stage4& b2, const Src& src,
-                                          int k0, int k1, int last, int wm0, int wn0,
-                                          const LoadMap& mp, int lane) {
-  int kt = k0;
-#define SYNC(k) (((k) & 1) != 0 || (k) == k1 - 1)
-  // bring kt to a multiple of 3
-  while (kt < k1 && kt % 3 != 0) {
-    if (kt % 3 == 1)
-      step<F16>(sm, acc, f0, f1, b2, b0, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
-    else
-      step<F16>(sm, acc, f0, f1, b0, b1, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
-    ++kt;
-  }
-  for (; kt + 3 <= k1; kt += 3) {
-    step<F16>(sm, acc, f0, f1, b1, b2, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
-    step<F16>(sm, acc, f0, f1, b2, b0, src, kt + 1, last, wm0, wn0, mp, lane, SYNC(kt + 1));
-    step<F16>(sm, acc, f0, f1, b0, b1, src, kt + 2, last, wm0, wn0, mp, lane, SYNC(kt + 2));
-  }
-  if (kt < k1) {
-    step<F16>(sm, acc, f0, f1, b1, b2, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
-    ++kt;
-  }
-  if (kt < k1) step<F16>(sm, acc, f0, f1, b2, b0, src, kt, last, wm0, wn0, mp, lane, SYNC(kt));
-#undef SYNC
-}
-
-// Pipeline prologue: steps 0, 1 and 2 into stages 0, 1 and 2 (through
-// buffers 0, 1 and 2), then the loads of steps 3 and 4 into buffers 2 and 0,
-// the first fragments of step 0.
-__device__ __forceinline__ void prologue(Smem& sm, Frag& f0, Stage4& b0, Stage4& b1, Stage4& b2,
-                                         const Src& src, int last, int wm0, int wn0,
-                                         const LoadMap& mp, int lane) {
-  gload_all(b0, src, 0, mp);
-  gload_all(b1, src, min(1, last), mp);
-  gload_all(b2, src, min(2, last), mp);
-  lwrite_all(sm, 0, b0, mp);
-  lwrite_all(sm, 1, b1, mp);
-  lwrite_all(sm, 2, b2, mp);
-  gload_all(b2, src, min(3, last), mp);
-  gload_all(b0, src, min(4, last), mp);
-  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (NS - 2), 0));
   __builtin_amdgcn_s_barrier();
-  fload(f0, sm, 0, 0, wm0, wn0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    mma1<F16>(acc[t >> 2][t & 3], f1.b[t & 3], f1.a[t >> 2]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < 8) {
+      fread1(f0, lds, nxt, p, 0, t);
+      __builtin_amdgcn_sched_barrier(0);
+    } else if (t & 1) {
+      gload(lds, p, gsa, sa, false, (t - 8) >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <bool F16>
+__device__ __forceinline__ void run_steps(char* lds, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
+                                          const Pipe& p, int k0, int k1) {
+  int kt = k0;
+  for (; kt + 2 <= k1; kt += 2) {
+    step<F16>(lds, acc, f0, f1, p, kt);
+    step<F16>(lds, acc, f0, f1, p, kt + 1);
+  }
+  if (kt < k1) step<F16>(lds, acc, f0, f1, p, kt);
+}
+
+// Pipeline prologue: loads of steps 0 .. NS-2 and the A half of step NS-1
+// (the steady state's lead), then step 0 landed everywhere and f0 holds its
+// sub-step 0.
+__device__ __forceinline__ void prologue(char* lds, Frag& f0, const Pipe& p) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const Blk a = blk(p, s, false);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) gload(lds, p, a, s, false, q);
+    if (s < NS - 1) {
+      const Blk b = blk(p, s, true);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) gload(lds, p, b, s, true, q);
+    }
+  }
+  // issued after step 0's loads: steps 1 .. NS-2 (8 each) and A of NS-1 (4)
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (NS - 2) + 4, 0));
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int n = 0; n < 8; ++n) fread1(f0, lds, 0, p, 0, n);
 }
 
 // Accumulator element r of lane `lane` for tile (i, j) holds C at row
@@ -290,56 +259,6 @@ __device__ __forceinline__ void prologue(Smem& sm, Frag& f0, Stage4& b0, Stage4&
 // lane owns one row and runs of 4 consecutive columns.
 __device__ __forceinline__ int acc_col(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-}
-
-// Stores one 32x64 row group of the wave block (fp32, accumulator layout)
-// as fp16 Y rows m_base .. m_base+31, columns n_base .. n_base+63, through
-// the wave's 4 KiB staging area ys: each lane writes its 4-column runs as
-// 8-byte pieces (piece k of row r at position k ^ 2*((r/2)%8), which spreads
-// the 32 rows of a write over the banks), then reads whole 16-byte pieces
-// back for 128-byte row-segment stores (whole cache lines).
-__device__ __forceinline__ void store_rows(const v16f (&y)[TJ], uint16_t* ys,
-                                           uint16_t* __restrict__ Y, int M, int N, int m_base,
-                                           int n_base, bool vec_store, int lane) {
-  const int row = lane & 31;
-  const int sw = 2 * ((row >> 1) & 7);
-#pragma unroll
-  for (int j = 0; j < TJ; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = j * 8 + q * 2 + (lane >> 5);
-      uint2 v;
-      v.x = (uint32_t)f2h(y[j][4 * q]) | ((uint32_t)f2h(y[j][4 * q + 1]) << 16);
-      v.y = (uint32_t)f2h(y[j][4 * q + 2]) | ((uint32_t)f2h(y[j][4 * q + 3]) << 16);
-      *reinterpret_cast<uint2*>(ys + row * WN + (k ^ sw) * 4) = v;
-    }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int c16 = lane & 7;
-  const int n_col = n_base + c16 * 8;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int rl = p * 8 + (lane >> 3);  // row within the 32-row group
-    const int m = m_base + rl;
-    const int pos = (2 * c16) ^ (2 * ((rl >> 1) & 7));  // even: the pair stays in order
-    const v4i v = *reinterpret_cast<const v4i*>(ys + rl * WN + pos * 4);
-    if (m < M) {
-      if (vec_store && n_col + 8 <= N) {
-        // Y is written once and not read again here: stream it past the
-        // caches (same HBM write bytes as plain stores, ~2% faster kernel)
-        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col));
-      } else {
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Tile of workgroup b, in an XCD-aware order: consecutive workgroups go
@@ -358,144 +277,121 @@ __device__ __forceinline__ void tile_of(int b, int M, int N, int& tm, int& tn) {
   tn = (L % per_group) / gsz;
 }
 
-}  // namespace
+// Stores rows m_base .. +31, columns n_base .. +127 of Y from y (fp32,
+// accumulator layout) through the wave's 8 KiB staging area ys: each lane
+// writes its 4-column runs as 8-byte pieces (piece e of row r at position
+// e ^ 2*((r/2)%16), which spreads the rows of a write over the banks), then
+// reads back whole 16-byte pieces for 256-byte row-segment stores.
+__device__ __forceinline__ void store_rows(const v16f (&y)[TJ], char* ys, uint16_t* __restrict__ Y,
+                                           int M, int N, int m_base, int n_base, bool vec,
+                                           int lane) {
+  const int row = lane & 31;
+  const int sw = 2 * ((row >> 1) & 15);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = j * 8 + q * 2 + (lane >> 5);
+      uint2 v;
+      v.x = (uint32_t)f2h(y[j][4 * q]) | ((uint32_t)f2h(y[j][4 * q + 1]) << 16);
+      v.y = (uint32_t)f2h(y[j][4 * q + 2]) | ((uint32_t)f2h(y[j][4 * q + 3]) << 16);
+      *reinterpret_cast<uint2*>(ys + row * 256 + (e ^ sw) * 8) = v;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int c16 = lane & 15;
+  const int n_col = n_base + c16 * 8;
+#pragma unroll
+  for (int pp = 0; pp < 8; ++pp) {
+    const int rl = pp * 4 + (lane >> 4);
+    const int m = m_base + rl;
+    const int pos = (2 * c16) ^ (2 * ((rl >> 1) & 15));  // even: the pair stays in order
+    const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 256 + pos * 8);
+    if (m < M) {
+      if (vec && n_col + 8 <= N) {
+        // Y is written once and not read again here: stream it past the caches
+        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col));
+      } else {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-// Many outlier columns (more than three fp16 steps).  The int8 steps run
-// through the pipeline as in the common path; then the int32 accumulators
-// are dequantized into fp32 accumulators and the fp16 steps follow in a
-// simpler loop of its own: one step per LDS stage (two stages alternating),
-// three register buffers so that each step's loads are issued two steps
-// before it is written to LDS, one barrier per step.  Kept out of line so
-// that its registers do not shape the common path's allocation.
-template <bool BIAS>
-__device__ __attribute__((noinline)) void gemm_tile_many_outliers(
-    Smem& sm, const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
-    int ldk,
-    const float* __restrict__ x_scale, const float* __restrict__ w_scale,
-    const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-    const int32_t* __restrict__ n_out, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ Y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave >> 2) * WM, wn0 = (wave & 3) * WN;
-  int tm, tn;
-  tile_of(blockIdx.x, M, N, tm, tn);
+// Many outlier columns (more than NS-1 fp16 steps): the whole tile in one
+// workgroup; the int8 steps, then the accumulators rescaled in place to fp32
+// (fp32(C)*s + b, the order of the few-outlier epilogue) and the fp16 steps
+// continued through the same pipeline.  With |O| = K every code is 0 and C =
+// 0: the int8 steps are skipped.  A branch of its own at the kernel's start,
+// so nothing of the common path is live in it.
+__device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restrict__ Xq,
+                                               const int8_t* __restrict__ Wq, int M, int N, int K,
+                                               int ldk, const uint16_t* __restrict__ XO,
+                                               const uint16_t* __restrict__ WO, int n_out,
+                                               uint16_t* __restrict__ Y, int tm, int tn) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
   const int m0 = tm * BM, n0 = tn * BN;
-
+  const float* s_x = reinterpret_cast<const float*>(lds + kScaleOff);
+  const float* s_w = s_x + BM;
+  const float* s_b = s_w + BN;
+  const int nk8 = ldk / kTileK;
+  const int nk16 = (n_out + 31) / 32;
+  const int n8 = n_out < K ? nk8 : 0;
+  Pipe p;
+  make_pipe(p, Xq, Wq, XO, WO, tm, tn, nk8, 0, n8, nk16, wave, lane);
   v16i acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
-
-  const int nk8 = ldk / kTileK;
-  const int nk16 = (*n_out + 31) / 32;
-  Src src;
-  src.A = (const char*)Xq + (size_t)tm * nk8 * kTileBytes;
-  src.B = (const char*)Wq + (size_t)tn * nk8 * kTileBytes;
-  src.AO = (const char*)XO + (size_t)tm * (2 * nk8) * kTileBytes;  // fp16 rows: 2*ldk bytes
-  src.BO = (const char*)WO + (size_t)tn * (2 * nk8) * kTileBytes;
-  src.nk8 = nk8;
-
-  const LoadMap mp = load_map(__builtin_amdgcn_readfirstlane(wave), lane);
-  Stage4 b0, b1, b2;
-  if (*n_out < K) {
-    // int8 part: the pipeline clamped to the int8 steps (with |O| = K every
-    // code is 0 and C = 0: skipped)
-    Frag f0, f1;
-    const int last8 = nk8 - 1;
-    prologue(sm, f0, b0, b1, b2, src, last8, wm0, wn0, mp, lane);
-    run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nk8, last8, wm0, wn0, mp, lane);
-  }
-
-  // fp32 accumulators: fp32(C) * a_x[m] * a_w[n] / 127^2 (+ b[n])
-  v16f yf[TI][TJ];
-  if constexpr (!BIAS) {
+  Frag f0, f1;
+  prologue(lds, f0, p);
+  run_steps<false>(lds, acc, f0, f1, p, 0, n8);
+  // one column quad at a time (its scales and biases read once, applied to
+  // the four row groups), so that few registers are live beside the
+  // accumulators
+  float sx[TI];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const float sx = x_scale[min(m0 + wm0 + i * 32 + (lane & 31), M - 1)];
+  for (int i = 0; i < TI; ++i) sx[i] = s_x[wm0 + i * 32 + (lane & 31)];
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+  for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float sw = w_scale[min(n0 + wn0 + j * 32 + acc_col(r, lane), N - 1)] * kInv127Sq;
-          yf[i][j][r] = (float)acc[i][j][r] * (sx * sw);
-        }
-    }
-  }
-
-  // fp16 steps st = 0 .. nk16-1 (pipeline steps nk8 + st): step st is in
-  // register buffer st % 3 and LDS stage st % 2
-  wait_all();
-  __syncthreads();  // every wave is done with the int8 stages
-  if constexpr (BIAS) {
-    // the tile's scales and bias go through stage NBUF-1 (the fp16 steps use
-    // stages 0 and 1): per-element global loads of the bias as well would
-    // spill registers
-    float* s_x = reinterpret_cast<float*>(&sm.a[NBUF - 1][0]);
-    float* s_w = s_x + BM;
-    float* s_b = s_w + BN;
-    if (threadIdx.x < BM) {
-      const int t = threadIdx.x;
-      s_x[t] = x_scale[min(m0 + t, M - 1)];
-      s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
-      s_b[t] = h2f(bias[min(n0 + t, N - 1)]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const float sx = s_x[wm0 + i * 32 + (lane & 31)];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
-          const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[c]);
-          const v4f b4 = *reinterpret_cast<const v4f*>(&s_b[c]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            yf[i][j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]) + b4[e];
-        }
-    }
-  }
-  gload_all(b0, src, nk8, mp);
-  if (nk16 > 1) gload_all(b1, src, nk8 + 1, mp);
-  if (nk16 > 2) gload_all(b2, src, nk8 + 2, mp);
-  lwrite_all(sm, 0, b0, mp);
-  __syncthreads();
-  auto f16_step = [&](int st, Stage4& ld, const Stage4& wr) {
-    if (st + 3 < nk16) gload_all(ld, src, nk8 + st + 3, mp);
-    const int buf = st & 1;
-    Frag f[2];  // both sub-steps' fragments read up front
-    fload(f[0], sm, buf, 0, wm0, wn0, lane);
-    fload(f[1], sm, buf, 1, wm0, wn0, lane);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int q = 0; q < 4; ++q) {
+      const int c = wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
+      const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[c]);
+      const v4f b4 = *reinterpret_cast<const v4f*>(&s_b[c]);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          yf[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, f[kk].b[j]),
-                                                            __builtin_bit_cast(v8h, f[kk].a[i]),
-                                                            yf[i][j], 0, 0, 0);
-    // stage (st+1) % 2 was last read in step st-1, before the last barrier
-    if (st + 1 < nk16) lwrite_all(sm, (st + 1) & 1, wr, mp);
-    __syncthreads();
-  };
-  int st = 0;
-  for (; st + 3 <= nk16; st += 3) {
-    f16_step(st, b0, b1);
-    f16_step(st + 1, b1, b2);
-    f16_step(st + 2, b2, b0);
-  }
-  if (st < nk16) f16_step(st, b0, b1);
-  if (st + 1 < nk16) f16_step(st + 1, b1, b2);
-
-  // store fp16 Y through LDS, 4 KiB per wave
-  const bool vec_store = (N & 7) == 0;
-  uint16_t* ys = reinterpret_cast<uint16_t*>(&sm.a[0][0]) + wave * (32 * WN);
+        for (int e = 0; e < 4; ++e)
+          acc[i][j][4 * q + e] =
+              __float_as_int((float)acc[i][j][4 * q + e] * (sx[i] * w4[e]) + b4[e]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  run_steps<true>(lds, acc, f0, f1, p, n8, n8 + nk16);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const bool vec = (N & 7) == 0;
+  char* ys = lds + wave * 8192;
 #pragma unroll
-  for (int i = 0; i < TI; ++i) store_rows(yf[i], ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
+  for (int i = 0; i < TI; ++i) {
+    v16f y[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) y[j] = __builtin_bit_cast(v16f, acc[i][j]);
+    store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
+  }
 }
+
+}  // namespace
 
 // nsplit (MODE 0 only): the last nsplit tiles (in workgroup order) are each
 // computed by two workgroups, unit u = 0 .. nsplit-1 as workgroups
@@ -506,15 +402,14 @@ __device__ __attribute__((noinline)) void gemm_tile_many_outliers(
 // an exact integer sum, and runs the epilogue.  Used when the tiles would
 // leave most of the GPU idle.
 template <int MODE>  // 0: Y (fused epilogue), 1: int32 C
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
 k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
-               int ldk,
-               const float* __restrict__ x_scale, const float* __restrict__ w_scale,
+               int ldk, const float* __restrict__ x_scale, const float* __restrict__ w_scale,
                const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
                const int32_t* __restrict__ n_out, const uint16_t* __restrict__ bias,
                uint16_t* __restrict__ Y, int32_t* __restrict__ C, int nsplit,
                int32_t* __restrict__ cpart, int32_t* __restrict__ ctr) {
-  __shared__ Smem sm;
+  __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int nwhole = tiles - nsplit;
   int tb = (int)blockIdx.x, half = 0, su = -1;  // su: split unit of this workgroup
@@ -525,23 +420,40 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     tb = nwhole + su;
   }
   const bool split = su >= 0;
-  if (MODE == 0 && (*n_out + 31) / 32 > 3) {
-    // whole tile in one workgroup (half 0 of a split unit is workgroup tb)
-    if (half == 0) {
-      if (bias != nullptr)
-        gemm_tile_many_outliers<true>(sm, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out,
-                                      bias, Y);
-      else
-        gemm_tile_many_outliers<false>(sm, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out,
-                                       nullptr, Y);
-    }
-    return;
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave >> 2) * WM, wn0 = (wave & 3) * WN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
   int tm, tn;
   tile_of(tb, M, N, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+
+  // the tile's scales (w_scale already divided by 127^2) and biases, read by
+  // the epilogue after the loop's barriers have published them
+  float* s_x = reinterpret_cast<float*>(lds + kScaleOff);
+  float* s_w = s_x + BM;
+  float* s_b = s_w + BN;
+  int* s_flag = reinterpret_cast<int*>(s_b + BN);
+  if (MODE == 0) {
+    const int t = threadIdx.x;
+    s_x[t] = x_scale[min(m0 + t, M - 1)];
+    s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
+    s_b[t] = bias != nullptr ? h2f(bias[min(n0 + t, N - 1)]) : 0.0f;
+  }
+
+  const int nk8 = ldk / kTileK;
+  const int nk16 = MODE == 0 ? (*n_out + 31) / 32 : 0;
+  if (MODE == 0 && nk16 > NS - 1) {
+    // whole tile in one workgroup (half 0 of a split unit is workgroup tb)
+    __syncthreads();  // the tile's scales are in LDS
+    if (half == 0) gemm_tile_many(lds, Xq, Wq, M, N, K, ldk, XO, WO, *n_out, Y, tm, tn);
+    return;
+  }
+  // this workgroup's int8 steps [k0, k0 + nr); pipeline step s < nr is int8
+  // step k0 + s, then come the outlier steps
+  const int k0 = half ? nk8 / 2 : 0;
+  const int nr = split ? (half ? nk8 - nk8 / 2 : nk8 / 2) : nk8;
+  Pipe p;
+  make_pipe(p, Xq, Wq, XO, WO, tm, tn, nk8, k0, nr, nk16, wave, lane);
 
   v16i acc[TI][TJ];
 #pragma unroll
@@ -549,36 +461,21 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
 
-  const int nk8 = ldk / kTileK;
-  const int nk16 = MODE == 0 ? (*n_out + 31) / 32 : 0;
-  // this workgroup's int8 steps [k0, k0 + nr); pipeline step s < nr is int8
-  // step k0 + s, then come the outlier steps
-  const int k0 = half ? nk8 / 2 : 0;
-  const int nr = split ? (half ? nk8 - nk8 / 2 : nk8 / 2) : nk8;
-  const int last = nr + nk16 - 1;
-  Src src;
-  src.A = (const char*)Xq + ((size_t)tm * nk8 + k0) * kTileBytes;
-  src.B = (const char*)Wq + ((size_t)tn * nk8 + k0) * kTileBytes;
-  src.AO = (const char*)XO + (size_t)tm * (2 * nk8) * kTileBytes;  // fp16 rows: 2*ldk bytes
-  src.BO = (const char*)WO + (size_t)tn * (2 * nk8) * kTileBytes;
-  src.nk8 = nr;
-
-  const LoadMap mp = load_map(__builtin_amdgcn_readfirstlane(wave), lane);
-  Stage4 b0, b1, b2;
   Frag f0, f1;
-  prologue(sm, f0, b0, b1, b2, src, last, wm0, wn0, mp, lane);
-
-  // ---- int8 x int8 -> int32 over this workgroup's K steps (outlier
-  // columns of Xq are zero)
-  run_steps<false>(sm, acc, f0, f1, b0, b1, b2, src, 0, nr, last, wm0, wn0, mp, lane);
+  prologue(lds, f0, p);
+  // int8 x int8 -> int32 over this workgroup's K steps (outlier columns of
+  // Xq are zero); the loads of the outlier steps ride along
+  run_steps<false>(lds, acc, f0, f1, p, 0, nr);
 
   if (MODE == 0 && split) {
     // partial of this half, four registers per pass: each lane stores 16
     // bytes, each wave 1 KiB contiguous
     constexpr int kQuads = TI * TJ * 4;
-    v4i* mine = reinterpret_cast<v4i*>(cpart) + ((size_t)su * 2 + half) * kQuads * NT + threadIdx.x;
+    v4i* mine =
+        reinterpret_cast<v4i*>(cpart) + ((size_t)su * 2 + half) * kQuads * NT + threadIdx.x;
     const v4i* other =
-        reinterpret_cast<const v4i*>(cpart) + ((size_t)su * 2 + (half ^ 1)) * kQuads * NT + threadIdx.x;
+        reinterpret_cast<const v4i*>(cpart) + ((size_t)su * 2 + (half ^ 1)) * kQuads * NT +
+        threadIdx.x;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -587,33 +484,43 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
         for (int q = 0; q < 4; ++q)
           mine[((i * TJ + j) * 4 + q) * NT] =
               v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-    // the flag lives in stage (nr+3) % NBUF, free since the loop's last
-    // barrier and overwritten by the epilogue only after its own barrier
-    int* s_first = reinterpret_cast<int*>(&sm.a[(nr + 3) % NBUF][0]);
-    wait_all();       // this thread's stores have landed
-    __syncthreads();  // ... and every other thread's
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores (and every load) have landed
+    __syncthreads();                // ... and every other thread's
     if (threadIdx.x == 0) {
       __threadfence();  // the partial is visible device-wide before the count
       const int first = atomicAdd(&ctr[su], 1) == 0;
       if (!first) __threadfence();  // and the other half's is seen after it
-      *s_first = first;
+      *s_flag = first;
     }
     __syncthreads();
-    if (*s_first) return;  // the other half finishes the tile
+    if (*s_flag) return;  // the other half finishes the tile
+    // the other half's partial in two batches of 32 loads per lane, each
+    // batch entirely in flight before its adds (one memory round trip per
+    // batch, not per load)
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int i0 = 0; i0 < TI; i0 += 2) {
+      v4i o[2][TJ][4];
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v4i o = other[((i * TJ + j) * 4 + q) * NT];
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += o[e];
-        }
+          for (int q = 0; q < 4; ++q) o[i][j][q] = other[(((i0 + i) * TJ + j) * 4 + q) * NT];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i0 + i][j][4 * q + e] += o[i][j][q][e];
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   if (MODE == 1) {
-    wait_all();
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -627,34 +534,18 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
     return;
   }
 
-  // Few outlier steps (at most 3): pipeline steps nr .. nr+2 were written to
-  // LDS stages (nr + s) % NBUF by the int8 loop.  Stages (nr + 3) % NBUF and
-  // (nr + 4) % NBUF held the last two int8 steps, whose reads ended at the
-  // last barrier (the last step of the loop ends with one): the tile's
-  // scales go to the second,
-  // fp16 Y is staged in the first (4 KiB per wave).  Per 32-row group i:
-  // Y = fp32(C)*s read straight from the int32 accumulators, the outlier
-  // product accumulated on top, converted to fp16 and stored as 128-byte row
-  // segments.
-  const bool vec_store = (N & 7) == 0;
-  float* s_x = reinterpret_cast<float*>(&sm.a[(nr + NBUF - 1) % NBUF][0]);
-  float* s_w = s_x + BM;
-  float* s_b = s_w + BN;
-  if (threadIdx.x < BM) {
-    const int t = threadIdx.x;
-    s_x[t] = x_scale[min(m0 + t, M - 1)];
-    s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
-    s_b[t] = bias != nullptr ? h2f(bias[min(n0 + t, N - 1)]) : 0.0f;
-  }
-  wait_all();
+  // Few outlier steps (at most NS-1): pipeline steps nr .. nr+nk16-1 sit in
+  // LDS stages (nr+st)%NS, loaded by the int8 loop; stage (nr-1)%NS, the last
+  // int8 step's, is free once every load has landed (the loads past the last
+  // step that targeted it fetched nothing) and stages Y (8 KiB per wave).  Per
+  // 32-row group i: Y = fp32(C)*s + b straight from the int32 accumulators,
+  // the outlier products accumulated on top, fp16 rows stored.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int fs = (nr + 3) % NBUF;
-  uint16_t* ys = reinterpret_cast<uint16_t*>(wave < 4 ? &sm.a[fs][0] : &sm.b[fs][0]) +
-                 (wave & 3) * (32 * WN);
+  const bool vec = (N & 7) == 0;
+  char* ys = lds + ((nr + NS - 1) & (NS - 1)) * kStage + wave * 8192;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
-    // row group i: scaled int8 part first (its accumulator registers are
-    // then free for the fp16 MFMAs), outlier products accumulated on top
     const float sx = s_x[wm0 + i * 32 + (lane & 31)];
     v16f y[TJ];
 #pragma unroll
@@ -669,19 +560,18 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
           y[j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]) + b4[e];
       }
     for (int st = 0; st < nk16; ++st) {
-      const int stg = (nr + st) % NBUF;
+      const uint32_t sb = (uint32_t)((nr + st) & (NS - 1)) * kStage;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int ch = kk * 2 + (lane >> 5);
-        const v8h a = __builtin_bit_cast(v8h, sm.a[stg][swz(wm0 + i * 32 + (lane & 31), ch)]);
+        const v8h a = __builtin_bit_cast(v8h, lread(lds, sb + p.ra[kk] + i * 2048));
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-          const v8h b = __builtin_bit_cast(v8h, sm.b[stg][swz(wn0 + j * 32 + (lane & 31), ch)]);
-          y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, y[j], 0, 0, 0);
+          const v8h bb = __builtin_bit_cast(v8h, lread(lds, sb + p.rb[kk] + j * 2048));
+          y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bb, a, y[j], 0, 0, 0);
         }
       }
     }
-    store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec_store, lane);
+    store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
   }
 }
 

@@ -29,6 +29,21 @@ SHAPES = [
     (5, 3, 7, 1, 6.0),
     (16, 520, 100, 4, 0.0),
     (9, 200, 33, 3, math.inf),
+    # the few-rows activation launch at each of its widths: 256 threads up to
+    # K = 2048, 1024 threads up to 8192, two chunks per thread up to 16384;
+    # past that the general mask and row passes
+    (1, 2056, 64, 2, 6.0),
+    (16, 8192, 48, 3, 6.0),
+    (16, 8200, 64, 3, 6.0),
+    (1, 16384, 40, 2, 6.0),
+    (16, 16384, 48, 4, 6.0),
+    (3, 16392, 40, 2, 6.0),
+    # decode grids that cover more 16-row groups than the prepared weight's
+    # padded rows hold (8704 rows: 546 groups launched for 544), and G = 3
+    # groups per workgroup not dividing the group count (11008 rows)
+    (1, 1024, 8704, 3, 6.0),
+    (16, 1024, 8704, 3, 6.0),
+    (16, 4096, 11008, 4, 6.0),
     # prefill path: M > 16
     (17, 1024, 1024, 2, 6.0),
     (300, 520, 300, 5, 6.0),
@@ -183,3 +198,21 @@ def test_maximum_k_at_the_int32_bound(lib, M, t):
     Y, Y_ref = run_case(lib, X, W, t)
     if t == math.inf:  # |C| = 127^2 K exactly (checked bit for bit by run_case): Y = fp16(K/4)
         assert np.all(np.abs(Y_ref) == np.float16(0.25 * K))
+
+
+def test_wrong_shaped_outputs_are_refused(lib):
+    import torch
+    X, W = _case(32, 128, 64, seed=21, n_out=2)
+    Xd, Wd = to_dev(X), to_dev(W)
+    Wq, s = lib.int8_prepare_weight(Wd)
+    with pytest.raises(ValueError, match="shape"):
+        lib.int8_matmul(Xd, Wq, s, out=torch.empty((32, 63), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError, match="shape"):
+        lib.int8_linear(Xd, Wq, s, out=torch.empty((31, 64), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError, match="shape"):
+        lib.int8_prepare_weight(Wd, out=(torch.empty((64, 128), dtype=torch.int8, device="cuda"), s))
+    with pytest.raises(ValueError, match="shape"):
+        lib.int8_prepare_weight(Wd, out=(torch.empty_like(Wq), torch.empty((63,), device="cuda")))
+    # the right shapes are accepted
+    Y = lib.int8_matmul(Xd, Wq, s, out=torch.empty((32, 64), dtype=torch.float16, device="cuda"))
+    assert Y.shape == (32, 64)

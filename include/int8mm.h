@@ -30,9 +30,10 @@
  *     failed check returns a negative status and enqueues nothing.
  *   - HIP launch failures return INT8MM_EHIP; the error text is available
  *     from int8mm_last_hip_error() on the calling thread.
- *   - No global mutable state: calls on different streams with different
- *     workspaces may run concurrently.  Two calls that share a workspace
- *     must be ordered (e.g. on one stream).
+ *   - No global mutable state (the one exception is the static workspace of
+ *     int8_matmul_noalloc, see there): calls on different streams with
+ *     different workspaces may run concurrently.  Two calls that share a
+ *     workspace must be ordered (e.g. on one stream).
  *   - A call can be captured in a HIP graph and replayed: it records only
  *     kernel launches (counters and fills are cleared by kernels, never by
  *     hipMemsetAsync), and every counter it relies on is cleared by an
@@ -73,6 +74,8 @@ typedef uint16_t int8mm_half;
 #define INT8MM_ESHAPE (-2)     /* negative dimension or K > INT8MM_MAX_K     */
 #define INT8MM_EWORKSPACE (-3) /* workspace null, too small or misaligned    */
 #define INT8MM_EHIP (-4)       /* a HIP launch failed                        */
+#define INT8MM_ESCRATCH (-5)   /* int8_matmul_noalloc: shape needs more
+                                  workspace than its static buffer holds     */
 
 /* Largest K for which every int32 accumulator |sum_k q_x q_w| <= 127*127*K
  * fits in int32 (127*127*133144 = 2147479576 < 2^31). */
@@ -219,6 +222,37 @@ INT8MM_API int int8_matmul_profiled(const int8mm_half* X, int64_t M, int64_t K,
                 float threshold, int8mm_half* Y,
                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                 hipEvent_t matmul_start, hipEvent_t matmul_stop);
+
+/*
+ * int8_matmul_noalloc -- int8_matmul for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results, with no workspace
+ * argument.  The workspace is a static device buffer of the library,
+ * INT8MM_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, reserved when the library's
+ * device code is loaded on that GPU and held until the process ends; the
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ *   Arguments, layouts, results and errors as int8_matmul, plus:
+ *   INT8MM_ESCRATCH  the shape needs more than the buffer holds, i.e.
+ *                    int8_matmul_workspace_size(M, K, N) >
+ *                    int8_matmul_noalloc_max_workspace() (checked on the host
+ *                    before anything is enqueued; decode shapes, M <= 16, fit
+ *                    for every K; prefill shapes fit up to about 40 MiB of
+ *                    X + outlier slices).
+ * Every call on one GPU uses that GPU's single buffer, which keeps the last
+ * call's contents: calls that overlap on one GPU (concurrent streams, or
+ * host threads) race and must be ordered by the caller.  Every counter the
+ * kernels rely on is cleared by an earlier kernel of the same call.
+ */
+#define INT8MM_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+INT8MM_API int int8_matmul_noalloc(const int8mm_half* X, int64_t M, int64_t K,
+                const int8_t* Wq, const float* w_scale, int64_t N,
+                float threshold, int8mm_half* Y, hipStream_t stream);
+
+/* Bytes of int8_matmul_noalloc's static workspace (the largest
+ * int8_matmul_workspace_size it accepts). */
+INT8MM_API size_t int8_matmul_noalloc_max_workspace(void);
 
 /* Static text for a status code. */
 INT8MM_API const char* int8mm_strerror(int status);

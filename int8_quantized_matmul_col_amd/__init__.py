@@ -25,6 +25,8 @@ from .binding import (  # noqa: F401
     int8_column_absmax,
     int8_linear,
     int8_matmul,
+    int8_matmul_noalloc,
+    int8_matmul_noalloc_max_workspace,
     int8_matmul_profiled,
     int8_matmul_stages,
     int8_matmul_workspace_size,

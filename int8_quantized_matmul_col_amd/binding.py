@@ -23,6 +23,7 @@ INT8MM_EINVAL = -1
 INT8MM_ESHAPE = -2
 INT8MM_EWORKSPACE = -3
 INT8MM_EHIP = -4
+INT8MM_ESCRATCH = -5
 INT8MM_MAX_K = 133144
 INT8MM_DECODE_MAX_M = 16
 
@@ -47,6 +48,8 @@ SIGNATURES = {
     "int8_matmul_stages": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float,
                                           _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, ctypes.c_size_t, _P]),
+    "int8_matmul_noalloc": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P]),
+    "int8_matmul_noalloc_max_workspace": (ctypes.c_size_t, []),
     "int8mm_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "int8mm_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -216,6 +219,35 @@ def int8_matmul(X, Wq, w_scale, threshold: float = DEFAULT_THRESHOLD, out=None, 
                          _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check("int8_matmul", st)
     return Y
+
+
+def int8_matmul_noalloc(X, Wq, w_scale, threshold: float = DEFAULT_THRESHOLD, out=None):
+    """int8_matmul through the library's static workspace (no workspace
+    argument, nothing allocated by the call; `out` preallocated when the
+    caller cannot allocate).  Shapes whose workspace exceeds
+    int8_matmul_noalloc_max_workspace() raise (INT8MM_ESCRATCH)."""
+    import torch
+    lib = load()
+    _require(X, torch.float16, "X")
+    dev = X.device
+    _require(Wq, torch.int8, "Wq", dev)
+    _require(w_scale, torch.float32, "w_scale", dev)
+    M, K = X.shape
+    N = w_scale.numel()
+    if Wq.numel() != int8_weight_bytes(N, K):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wq {tuple(Wq.shape)}, "
+                         f"w_scale {tuple(w_scale.shape)}")
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=dev)
+    if out is not None:
+        _check_out(Y, (M, N), torch.float16, "out", dev)
+    st = lib.int8_matmul_noalloc(_ptr(X), M, K, _ptr(Wq), _ptr(w_scale), N, float(threshold),
+                                 _ptr(Y), _stream(dev))
+    _check("int8_matmul_noalloc", st)
+    return Y
+
+
+def int8_matmul_noalloc_max_workspace() -> int:
+    return int(load().int8_matmul_noalloc_max_workspace())
 
 
 def int8_linear(X, Wq, w_scale, bias=None, threshold: float = DEFAULT_THRESHOLD, out=None,

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "int8mm.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -279,6 +281,64 @@ INT8MM_API int int8_column_absmax(const int8mm_half* X, int64_t M, int64_t K,
   return INT8MM_OK;
 }
 
+// ---- allocation-free variant of int8_matmul: the workspace is this file's
+// static device array, one copy per GPU (held until the process ends).  Host
+// code never passes the array's name (a host-side stand-in): its device
+// address is looked up once per device and cached.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)INT8MM_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, or nullptr with the
+// HIP error recorded.
+void* scratch_on_current_device(int* status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = hip_fail(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = INT8MM_EINVAL;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      *status = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+INT8MM_API int int8_matmul_noalloc(const int8mm_half* X, int64_t M, int64_t K, const int8_t* Wq,
+                                   const float* w_scale, int64_t N, float threshold,
+                                   int8mm_half* Y, hipStream_t stream) {
+  // the size check runs before anything touches the device
+  int st = check_shape(M, K, N);
+  if (st != INT8MM_OK) return st;
+  const size_t need = make_layout(M, K, N).total;
+  if (need > kScratchBytes) return INT8MM_ESCRATCH;
+  void* ws = scratch_on_current_device(&st);
+  if (ws == nullptr) return st;
+  Outputs out;
+  out.Y = Y;
+  return run(X, M, K, Wq, w_scale, N, threshold, out, false, ws, kScratchBytes, stream);
+}
+
+INT8MM_API size_t int8_matmul_noalloc_max_workspace(void) { return kScratchBytes; }
+
 INT8MM_API int int8_matmul_profiled(const int8mm_half* X, int64_t M, int64_t K, const int8_t* Wq,
                                     const float* w_scale, int64_t N, float threshold,
                                     int8mm_half* Y, void* workspace, size_t workspace_bytes,
@@ -315,6 +375,9 @@ INT8MM_API const char* int8mm_strerror(int status) {
     case INT8MM_ESHAPE: return "invalid shape (negative dimension or K above the int32 bound)";
     case INT8MM_EWORKSPACE: return "workspace missing, misaligned or too small";
     case INT8MM_EHIP: return "HIP launch failed";
+    case INT8MM_ESCRATCH:
+      return "shape needs more workspace than int8_matmul_noalloc holds "
+             "(int8_matmul_workspace_size > int8_matmul_noalloc_max_workspace)";
     default: return "unknown status";
   }
 }

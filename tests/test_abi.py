@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
     fns = header_functions()
     assert fns == sorted(["int8_weight_ld", "int8_weight_bytes", "int8_prepare_weight", "int8_matmul_workspace_size",
                           "int8_matmul", "int8_linear", "int8_matmul_stages", "int8_matmul_profiled",
-                          "int8_column_absmax", "int8mm_strerror", "int8mm_last_hip_error"])
+                          "int8_column_absmax", "int8mm_strerror", "int8mm_last_hip_error",
+                          "int8_matmul_noalloc", "int8_matmul_noalloc_max_workspace"])
     assert set(fns) == set(binding.SIGNATURES)
 
 
@@ -58,6 +59,7 @@ def test_header_constants_match_binding():
     assert int(consts["INT8MM_ESHAPE"]) == binding.INT8MM_ESHAPE
     assert int(consts["INT8MM_EWORKSPACE"]) == binding.INT8MM_EWORKSPACE
     assert int(consts["INT8MM_EHIP"]) == binding.INT8MM_EHIP
+    assert int(consts["INT8MM_ESCRATCH"]) == binding.INT8MM_ESCRATCH
     assert int(consts["INT8MM_MAX_K"]) == binding.INT8MM_MAX_K
     assert int(consts["INT8MM_DECODE_MAX_M"]) == binding.INT8MM_DECODE_MAX_M
 

@@ -1,6 +1,6 @@
 """Benchmark of the decomposed int8 matmul on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config q_proj] [--threshold T]
+    python bench.py [--steps K] [--warmup W] [--config sweep13b] [--extra q_proj,decode16]
 
 One step = one whole int8_matmul call (activation pass: outlier detection,
 row quantization and compaction; int8 MFMA GEMM; fp16 outlier MFMA; fused
@@ -9,8 +9,17 @@ prepared once before timing (int8_prepare_weight; its time is reported
 separately: the first call, and in ``prepare_weight`` the steady-state rate
 of 10 more calls against HBM bandwidth).  Prints one JSON line.
 
-* value     -- effective TOPS = 2*M*N*K / (wall time of K steps / K).
-* roofline  -- the matmul kernel alone: algorithmic work per launch divided by
+* headline   -- the LLaMA-13B-shaped sweep workload at t = 6 (4096 tokens,
+               5120 -> 13824), the largest single-GPU workload; ``extra``
+               holds the same measurement, in the same process, for the 7B
+               q_proj prefill (4096^3) and the M = 16 decode call
+               (8192 -> 28672), so both halves of the metric (% int8 MFMA
+               peak, % HBM bandwidth) are timed in one run.
+* value      -- effective TOPS = 2*M*N*K / (wall time of K steps / K).
+* weights    -- every workload cycles through enough prepared weight copies
+               (at least 768 MiB in all, so three times the 256 MB MALL) that
+               each call reads its weight from HBM, as a model's layers do.
+* roofline   -- the matmul kernel alone: algorithmic work per launch divided by
                its average duration, read from the HIP events its dispatch
                stamps (int8_matmul_profiled) over K calls run right after
                the timed region, on the same stream and inputs.  Prefill shapes are
@@ -18,18 +27,18 @@ of 10 more calls against HBM bandwidth).  Prints one JSON line.
                by HBM (8 TB/s); traffic comes from the committed rocprofv3
                FETCH_SIZE / WRITE_SIZE counters when they match the current
                kernel sources, else null.
-* warm-up   -- W calls, continued until it has lasted at least 50 ms
+* warm-up    -- W calls, continued until it has lasted at least 50 ms
                (warmup_calls_run says how many ran): the clocks need that long
                under load to settle, and value is the steady-state rate.
-* other_entry_points -- the same workload through int8_linear (with a
-               bias) and int8_column_absmax, K calls each after the timed
-               region.
-* per_call  -- median and minimum of per-call times (HIP events around each
+* other_entry_points -- the headline workload through int8_linear (with a
+               bias) and int8_column_absmax, after the timed region.
+* per_call   -- median and minimum of per-call times (HIP events around each
                whole call, and the kernel's own stamps), from passes after
                the timed region.
-* cpu_baseline -- the CPU oracle (oracle/, unchanged) timed on this host on
-               the same workload (or a row sample of it for the largest
-               ones), in the same unit.
+* cpu_baseline -- the CPU oracle (oracle/, unchanged) timed on this host: on a
+               row sample of the headline workload with all BLAS threads, and
+               single-threaded on the tiny and the M = 16 decode workloads; the
+               host's CPU count and the BLAS build are reported beside it.
 """
 
 from __future__ import annotations
@@ -197,91 +206,103 @@ def ingest_pmc(config: str, fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
-def cpu_baseline(case, threshold: float, budget_s: float = 20.0):
-    """The oracle, as it stands, on this host: one warm-up call then timed
-    calls until about `budget_s` seconds (at most 5).  Very large workloads
-    are sampled by rows (the unit is work per second, so it scales)."""
+def _blas_info():
+    """BLAS threads in use and the BLAS build numpy links."""
     import numpy as np
-    from oracle import int8mm_ref as ref
+    threads, build = os.cpu_count() or 1, "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        info = threadpool_info()
+        if info:
+            threads = max(i.get("num_threads", 1) for i in info)
+            build = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in info)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
-    M = case.M
-    rows = M if M * case.K * case.N <= 4096 * 5120 * 13824 // 2 else M // 4
-    X = case.X[:rows]
-    Wq, s = ref.prepare_weight_ref(case.W)
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        build = f"{blas.get('name')} {blas.get('version')} ({build})"
+    except Exception:  # pragma: no cover
+        pass
+    return int(threads), build
+
+
+def _time_oracle(X, Wq, s, threshold, n_max, budget_s):
+    import numpy as np
+    from oracle import int8mm_ref as ref
     ref.int8_matmul_ref(X, Wq, s, threshold)  # warm-up
     times = []
     t_start = time.perf_counter()
-    while len(times) < 5 and (time.perf_counter() - t_start) < budget_s:
+    while len(times) < n_max and (time.perf_counter() - t_start) < budget_s:
         t0 = time.perf_counter()
         ref.int8_matmul_ref(X, Wq, s, threshold)
         times.append(time.perf_counter() - t0)
-    med = float(np.median(times))
-    return {
+    return float(np.median(times)), len(times)
+
+
+def cpu_baseline(case, threshold: float, single_cases=(), budget_s: float = 15.0):
+    """The oracle, as it stands, on this host: one warm-up call then timed
+    calls until about `budget_s` seconds (at most 3, median).  The headline
+    workload is sampled by rows with all BLAS threads (the unit is work per
+    second, so it scales); `single_cases` ((name, case) pairs, whole) are
+    timed with one BLAS thread."""
+    from oracle import int8mm_ref as ref
+    threads, build = _blas_info()
+    M = case.M
+    rows = M if M * case.K * case.N <= 4096 * 5120 * 13824 // 4 else M // 8
+    X = case.X[:rows]
+    Wq, s = ref.prepare_weight_ref(case.W)
+    med, n = _time_oracle(X, Wq, s, threshold, 3, budget_s)
+    out = {
         "value": 2.0 * rows * case.N * case.K / med / 1e12,
         "unit": "TOPS",
         "cores": int(threads),
+        "host_cpus": os.cpu_count(),
+        "blas": build,
         "kind": "oracle",
         "sample": f"{rows} of {M} rows x K={case.K} x N={case.N}, threshold {threshold}; "
-                  f"median of {len(times)} timed calls after 1 warm-up ({med:.3f} s each); "
-                  f"numpy/OpenBLAS with {threads} threads",
+                  f"median of {n} timed calls after 1 warm-up ({med:.3f} s each); "
+                  f"{threads} BLAS threads",
+        "single_thread": {},
     }
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    for name, c in single_cases:
+        Wq1, s1 = ref.prepare_weight_ref(c.W)
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                med1, n1 = _time_oracle(c.X, Wq1, s1, c.threshold, 3, budget_s)
+        else:  # pragma: no cover
+            med1, n1 = _time_oracle(c.X, Wq1, s1, c.threshold, 3, budget_s)
+        out["single_thread"][name] = {
+            "value": 2.0 * c.M * c.N * c.K / med1 / 1e12, "unit": "TOPS", "cores": 1,
+            "seconds_per_call": round(med1, 4),
+            "sample": f"whole workload {c.M}x{c.K}x{c.N}, median of {n1} timed calls after 1 warm-up"}
+    return out
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="q_proj")
-    ap.add_argument("--threshold", type=float, default=None)
-    ap.add_argument("--rotate", type=int, default=None,
-                    help="weight copies cycled through (default: enough to exceed the 256 MB MALL)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after timing, run a copy-like elementwise kernel (torch.neg) over "
-                         f"{COPY_CAL_BYTES >> 20} MiB so HBM counters can be scaled to known bytes")
-    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="CPU only: read two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
-                         "WRITE_SIZE, both with --copy-calibration) and record the matmul kernel's "
-                         "HBM bytes per launch in profiles/traffic.json")
-    args = ap.parse_args()
-    if args.ingest_pmc:
-        return ingest_pmc(args.config, *args.ingest_pmc)
+# Prepared weight bytes every workload cycles through: three times the 256 MB
+# MALL, so that each call reads its weight from HBM.
+ROTATE_BYTES = 3 * 256 * 2 ** 20
+MAX_COPIES = 64
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        return 2
 
+def measure(mm, lib, ev, dev, case, t, steps, warmup, rotate=None, others=False,
+            copy_calibration=False):
+    """One workload: weight preparation, warm-up, the timed region of
+    `steps` whole calls, then the kernel-stamped and per-call passes.
+    Returns the measurement as a dict."""
     import numpy as np
     import torch
 
-    import int8_quantized_matmul_col_amd as mm
-    import workloads
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    lib = mm.load()
-
-    case = workloads.config_case(args.config)
-    t = case.threshold if args.threshold is None else args.threshold
     M, K, N = case.M, case.K, case.N
-    log(f"[bench] {args.config}: M={M} K={K} N={N} t={t}")
-
     X = torch.from_numpy(case.X).to(dev)
     W = torch.from_numpy(case.W).to(dev)
     ldk = mm.int8_weight_ld(K)
-    wq_bytes = N * ldk
-    n_copies = args.rotate if args.rotate else max(1, -(-3 * 256 * 2 ** 20 // wq_bytes))
-    n_copies = min(n_copies, 8)
-    ev = HipEvents()
+    wq_bytes = mm.int8_weight_bytes(N, K)
+    n_copies = rotate if rotate else max(1, -(-ROTATE_BYTES // wq_bytes))
+    n_copies = min(n_copies, MAX_COPIES)
     p0, p1 = ev.create(), ev.create()
     stream = torch.cuda.current_stream(dev).cuda_stream
     ev.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -339,27 +360,27 @@ def main() -> int:
     # sustained work to settle, and the rate reported is the steady one
     w0 = time.perf_counter()
     n_warm = 0
-    while n_warm < args.warmup or time.perf_counter() - w0 < WARMUP_MIN_S:
+    while n_warm < warmup or time.perf_counter() - w0 < WARMUP_MIN_S:
         step(n_warm)
         n_warm += 1
-        if n_warm >= args.warmup and n_warm % 16 == 0:
+        if n_warm >= warmup and n_warm % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # timed region: K plain calls
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / steps
 
     # the same K calls again through int8_matmul_profiled: the matmul kernel's
     # dispatch stamps a pair of HIP events per call (kept out of the timed
     # region above, since the event packets add time between launches)
-    evs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    evs = [(ev.create(), ev.create()) for _ in range(steps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         step_prof(i, *evs[i])
     torch.cuda.synchronize()
     kern_ms = [ev.elapsed_ms(a, b) for (a, b) in evs]
@@ -367,7 +388,7 @@ def main() -> int:
     # and once more with a HIP event pair around each whole call, for the
     # per-call median and minimum (the events add gaps: not the timed value)
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         ev.hip.hipEventRecord(evs[i][0], stream)
         step(i)
         ev.hip.hipEventRecord(evs[i][1], stream)
@@ -380,11 +401,12 @@ def main() -> int:
                 "call_ms_min": round(float(np.min(call_ms)), 5),
                 "kernel_ms_median": round(float(np.median(kern_ms)), 5),
                 "kernel_ms_min": round(float(np.min(kern_ms)), 5),
-                "timing": f"HIP events per call over {args.steps} calls after the timed region"}
+                "timing": f"HIP events per call over {steps} calls after the timed region"}
     ev.destroy(p0)
     ev.destroy(p1)
-    assert torch.isfinite(Y).all().item() or args.config == "tiny", "non-finite output"
-    if args.copy_calibration:
+    if not torch.isfinite(Y).all().item():
+        raise RuntimeError("non-finite output")
+    if copy_calibration:
         src = torch.ones(COPY_CAL_BYTES // 2, dtype=torch.float16, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -392,46 +414,49 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    # the other entry points on the same workload, after the timed region:
-    # the layer forward with a bias (int8_linear) in rounds interleaved with
-    # int8_matmul (so that both see the same clock), and the column maxima
-    # (int8_column_absmax)
-    bias = (torch.arange(N, device=dev, dtype=torch.float32) % 7 - 3).to(torch.float16) / 8
-    lin, cmx = lib.int8_linear, lib.int8_column_absmax
-    cm = torch.empty((K,), dtype=torch.float16, device=dev)
+    res = {}
+    if others:
+        # the other entry points on the same workload, after the timed region:
+        # the layer forward with a bias (int8_linear) in rounds interleaved
+        # with int8_matmul (so that both see the same clock), and the column
+        # maxima (int8_column_absmax)
+        bias = (torch.arange(N, device=dev, dtype=torch.float32) % 7 - 3).to(torch.float16) / 8
+        lin, cmx = lib.int8_linear, lib.int8_column_absmax
+        cm = torch.empty((K,), dtype=torch.float16, device=dev)
 
-    def step_lin(i):
-        wp, sp = args_w[i % len(args_w)]
-        st = lin(xp, M, K, wp, sp, N, bias.data_ptr(), float(t), yp, ws_ptr, ws_bytes, stream)
-        if st != 0:
-            raise mm.Int8mmError("int8_linear", st)
+        def step_lin(i):
+            wp, sp = args_w[i % len(args_w)]
+            st = lin(xp, M, K, wp, sp, N, bias.data_ptr(), float(t), yp, ws_ptr, ws_bytes, stream)
+            if st != 0:
+                raise mm.Int8mmError("int8_linear", st)
 
-    def step_cmx(i):
-        st = cmx(xp, M, K, cm.data_ptr(), ws_ptr, ws_bytes, stream)
-        if st != 0:
-            raise mm.Int8mmError("int8_column_absmax", st)
+        def step_cmx(i):
+            st = cmx(xp, M, K, cm.data_ptr(), ws_ptr, ws_bytes, stream)
+            if st != 0:
+                raise mm.Int8mmError("int8_column_absmax", st)
 
-    def timed(fn, n):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(n):
-            fn(i)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / n
+        def timed(f, n):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            for i in range(n):
+                f(i)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - a) * 1e3 / n
 
-    n_round = max(1, min(args.steps, 20))
-    mm_ms, lin_ms = [], []
-    for _ in range(4):
-        mm_ms.append(timed(step, n_round))
-        lin_ms.append(timed(step_lin, n_round))
-    colmax_ms = timed(step_cmx, args.steps)
-    others = {"int8_linear_ms": round(float(np.median(lin_ms)), 5),
-              "int8_matmul_ms_same_rounds": round(float(np.median(mm_ms)), 5),
-              "int8_column_absmax_ms": round(colmax_ms, 5),
-              "column_absmax_GB/s": round(M * K * 2 / (colmax_ms * 1e-3) / 1e9, 1),
-              "timing": (f"wall clock; int8_linear (with a bias) and int8_matmul in 4 interleaved "
-                         f"rounds of {n_round} calls (medians), int8_column_absmax over "
-                         f"{args.steps} calls; all after the timed region")}
+        n_round = max(1, min(steps, 20))
+        mm_ms, lin_ms = [], []
+        for _ in range(4):
+            mm_ms.append(timed(step, n_round))
+            lin_ms.append(timed(step_lin, n_round))
+        colmax_ms = timed(step_cmx, steps)
+        res["other_entry_points"] = {
+            "int8_linear_ms": round(float(np.median(lin_ms)), 5),
+            "int8_matmul_ms_same_rounds": round(float(np.median(mm_ms)), 5),
+            "int8_column_absmax_ms": round(colmax_ms, 5),
+            "column_absmax_GB/s": round(M * K * 2 / (colmax_ms * 1e-3) / 1e9, 1),
+            "timing": (f"wall clock; int8_linear (with a bias) and int8_matmul in 4 interleaved "
+                       f"rounds of {n_round} calls (medians), int8_column_absmax over "
+                       f"{steps} calls; all after the timed region")}
 
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
@@ -441,48 +466,137 @@ def main() -> int:
         # matmul kernel algorithmic bytes: Wq + a_w + Xq + a_x + Y
         alg_bytes = N * K + 4 * N + M * K + 4 * M + 2 * M * N
         achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes_per_launch": alg_bytes}
+        call_gbs = alg_bytes / (ms_per_step * 1e-3) / 1e9
+        res["whole_call_hbm"] = {"GB/s": round(call_gbs, 1), "frac": round(call_gbs / PEAK_HBM_GBS, 4)}
     else:
         achieved = ops / (kern_avg * 1e-3) / 1e12
         peak = PEAK_FP16_TOPS if n_out == K else PEAK_INT8_TOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
-    roof["traffic"] = committed_traffic(args.config, src_hash)
+                "frac": round(achieved / peak, 4), "algorithmic_ops_per_launch": ops}
+    roof["traffic"] = committed_traffic(case.name, src_hash)
     roof["kernel"] = "k_gemm_decode" if decode else "k_gemm_prefill"
     roof["kernel_ms"] = round(kern_avg, 5)
-    roof["kernel_timing"] = (f"HIP events stamped by the {roof['kernel']} dispatch, mean of {args.steps} "
+    roof["kernel_timing"] = (f"HIP events stamped by the {roof['kernel']} dispatch, mean of {steps} "
                              "calls run right after the timed region")
+    res.update({
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "ms_per_step": round(ms_per_step, 5),
+        "warmup_calls_run": n_warm,
+        "config": {"workload": WORKLOAD_TEXT.get(case.name, case.name), "name": case.name,
+                   "M": M, "K": K, "N": N, "threshold": t, "n_outliers": n_out,
+                   "weight_copies": n_copies,
+                   "weight_bytes_rotated": n_copies * wq_bytes,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "per_call": per_call,
+        "prepare_weight_ms": round(prepare_ms, 4),
+        "prepare_weight": prepare,
+    })
+    del weights, X, Y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", default="sweep13b")
+    ap.add_argument("--extra", default="q_proj,decode16",
+                    help="workloads measured after the headline in the same run ('none': only "
+                         "the headline)")
+    ap.add_argument("--threshold", type=float, default=None)
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="weight copies cycled through (default: at least 768 MiB of weights, "
+                         "so that every call reads its weight from HBM)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a copy-like elementwise kernel (torch.neg) over "
+                         f"{COPY_CAL_BYTES >> 20} MiB so HBM counters can be scaled to known bytes")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="CPU only: read two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE, both with --copy-calibration and --extra none) and record "
+                         "the matmul kernel's HBM bytes per launch in profiles/traffic.json")
+    args = ap.parse_args()
+    if args.ingest_pmc:
+        return ingest_pmc(args.config, *args.ingest_pmc)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import int8_quantized_matmul_col_amd as mm
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = mm.load()
+    ev = HipEvents()
+
+    case = workloads.config_case(args.config)
+    t = case.threshold if args.threshold is None else args.threshold
+    log(f"[bench] {args.config}: M={case.M} K={case.K} N={case.N} t={t}")
+    head = measure(mm, lib, ev, dev, case, t, args.steps, args.warmup, args.rotate, others=True,
+                   copy_calibration=args.copy_calibration)
+    log(f"[bench] {args.config}: {head['ms_per_step']} ms per call, kernel "
+        f"{head['roofline']['kernel_ms']} ms, frac {head['roofline']['frac']}")
+
+    extra = {}
+    cases = {args.config: case}
+    names = [] if args.extra in ("", "none") else [n for n in args.extra.split(",") if n]
+    for name in names:
+        if name == args.config:
+            continue
+        c = cases[name] = workloads.config_case(name)
+        log(f"[bench] extra {name}: M={c.M} K={c.K} N={c.N} t={c.threshold}")
+        r = measure(mm, lib, ev, dev, c, c.threshold, args.steps, args.warmup, args.rotate)
+        r["metric"] = METRIC
+        extra[name] = r
+        log(f"[bench] {name}: {r['ms_per_step']} ms per call, kernel {r['roofline']['kernel_ms']} ms, "
+            f"frac {r['roofline']['frac']}")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
-        cpu = cpu_baseline(case, t)
+        singles = []
+        for name in ("tiny", "decode16"):
+            singles.append((name, cases.get(name) or workloads.config_case(name)))
+        cpu = cpu_baseline(case, t, singles)
 
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_calls_run": n_warm,
-        "ms_per_step": round(ms_per_step, 5),
+        "warmup_calls_run": head["warmup_calls_run"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded N(0,1) activations with planted outlier columns, N(0,0.02) weights)",
-        "config": {"workload": WORKLOAD_TEXT.get(args.config, args.config), "name": args.config,
-                   "M": M, "K": K, "N": N, "threshold": t, "n_outliers": n_out,
-                   "weight_copies": n_copies, "parallelism": "none (1 GPU)"},
-        "roofline": roof,
+        "config": head["config"],
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
-        "per_call": per_call,
-        "prepare_weight_ms": round(prepare_ms, 4),
-        "prepare_weight": prepare,
-        "other_entry_points": others,
-        "kernel_source_hash": src_hash,
+        "per_call": head["per_call"],
+        "prepare_weight_ms": head["prepare_weight_ms"],
+        "prepare_weight": head["prepare_weight"],
+        "other_entry_points": head.get("other_entry_points"),
+        "extra": extra,
+        "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -114,6 +114,28 @@ INT8MM_API int int8_prepare_weight(const int8mm_half* W, int64_t N, int64_t K,
                         int8_t* Wq, float* w_scale, hipStream_t stream);
 
 /*
+ * int8_pack_weight -- an already-quantized weight into the prepared form.
+ * ("PyTorch 2.9 supports LLM.int8()", section 1: the stored 8-bit weight is
+ * its int8 codes with one scale per output channel.)  For callers that hold
+ * the codes and scales of an absmax/127 per-channel quantization instead of
+ * the float16 W.
+ *
+ *   Wq_rowmajor [N][K] int8 codes, row-major (row n = output channel n).
+ *                      Codes are read as the method's range [-127, 127]; a
+ *                      code of -128 is stored as -127 (the int32 bound of
+ *                      INT8MM_MAX_K assumes |code| <= 127).
+ *   Wq          int8_weight_bytes(N, K) bytes out, panel-tiled [Np][ldk] as
+ *                      from int8_prepare_weight; padding rows and columns 0.
+ * The scales are not touched: pass them to int8_matmul as w_scale, as the
+ * channel absmax a_w[n] (so that W ~ Wq * a_w / 127).  For codes produced by
+ * int8_prepare_weight (unpacked) the output is byte-identical to its Wq.
+ * N == 0 or K == 0: nothing to do.  Errors: EINVAL (null pointer, Wq not
+ * 16-byte aligned), ESHAPE, EHIP.
+ */
+INT8MM_API int int8_pack_weight(const int8_t* Wq_rowmajor, int64_t N, int64_t K,
+                     int8_t* Wq, hipStream_t stream);
+
+/*
  * Bytes of device workspace int8_matmul / int8_matmul_stages need for this
  * shape (sized for the worst case |O| = K).  Returns 0 for an invalid shape.
  * The workspace must be 256-byte aligned.  Its contents on entry do not

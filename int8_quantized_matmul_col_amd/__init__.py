@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     int8_matmul_profiled,
     int8_matmul_stages,
     int8_matmul_workspace_size,
+    int8_pack_weight,
     int8_prepare_weight,
     int8_weight_bytes,
     int8_weight_ld,

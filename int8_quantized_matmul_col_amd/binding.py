@@ -37,6 +37,7 @@ SIGNATURES = {
     "int8_weight_ld": (ctypes.c_int64, [_I64]),
     "int8_weight_bytes": (ctypes.c_int64, [_I64, _I64]),
     "int8_prepare_weight": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "int8_pack_weight": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
     "int8_matmul_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "int8_matmul": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P,
                                    ctypes.c_size_t, _P]),
@@ -185,6 +186,25 @@ def int8_prepare_weight(W, out: Optional[Tuple] = None):
     st = lib.int8_prepare_weight(_ptr(W), N, K, _ptr(Wq), _ptr(ws), _stream(W.device))
     _check("int8_prepare_weight", st)
     return Wq, ws
+
+
+def int8_pack_weight(codes, out=None):
+    """codes: int8 [N][K] row-major (an absmax/127 per-channel quantization,
+    values in [-127, 127]) -> the prepared weight Wq int8 [Np][ldk]
+    (panel-tiled), for use with the caller's own per-channel scales."""
+    import torch
+    lib = load()
+    _require(codes, torch.int8, "codes")
+    if codes.dim() != 2:
+        raise ValueError("codes must be 2-D [N][K]")
+    N, K = codes.shape
+    Wq = out if out is not None else torch.empty((padded_rows(N), int8_weight_ld(K)),
+                                                 dtype=torch.int8, device=codes.device)
+    if out is not None:
+        _check_out(Wq, (padded_rows(N), int8_weight_ld(K)), torch.int8, "out", codes.device)
+    st = lib.int8_pack_weight(_ptr(codes), N, K, _ptr(Wq), _stream(codes.device))
+    _check("int8_pack_weight", st)
+    return Wq
 
 
 def workspace_for(M: int, K: int, N: int, device):

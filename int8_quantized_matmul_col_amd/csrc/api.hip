@@ -227,6 +227,17 @@ INT8MM_API int int8_prepare_weight(const int8mm_half* W, int64_t N, int64_t K, i
   return INT8MM_OK;
 }
 
+INT8MM_API int int8_pack_weight(const int8_t* Wq_rowmajor, int64_t N, int64_t K, int8_t* Wq,
+                                hipStream_t stream) {
+  if (N < 0 || K < 0 || K > INT8MM_MAX_K || N > kMaxRows) return INT8MM_ESHAPE;
+  if (N == 0 || K == 0) return INT8MM_OK;
+  if (Wq_rowmajor == nullptr || Wq == nullptr) return INT8MM_EINVAL;
+  if (!aligned16(Wq)) return INT8MM_EINVAL;
+  hipError_t e = i8mm::launch_pack_weight(Wq_rowmajor, (int)N, (int)K, (int)ld_of(K), Wq, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return INT8MM_OK;
+}
+
 INT8MM_API size_t int8_matmul_workspace_size(int64_t M, int64_t K, int64_t N) {
   if (check_shape(M, K, N) != INT8MM_OK) return 0;
   return make_layout(M, K, N).total;

@@ -14,6 +14,10 @@ constexpr int kColmaxRowsPerChunk = 64;
 
 hipError_t launch_prepare_weight(const uint16_t* W, int N, int K, int ldk, int8_t* Wq,
                                  float* w_scale, hipStream_t s);
+// Row-major int8 codes [N][K] into the panel-tiled layout (clamped to +-127,
+// zero padding).
+hipError_t launch_pack_weight(const int8_t* src, int N, int K, int ldk, int8_t* Wq,
+                              hipStream_t s);
 
 // Prefill: per-chunk column absmax partials part[rc][ldk] (u16 |x| bits).
 hipError_t launch_colmax_partial(const uint16_t* X, int M, int K, int ldk, uint16_t* part,

@@ -150,6 +150,47 @@ static bool launch_regs(const uint16_t* W, int N, int K, int ldk, int vec, int8_
   return true;
 }
 
+// ---------------------------------------------------------------- packing
+
+// Already-quantized weights ("PyTorch 2.9 supports LLM.int8()", section 1: the
+// stored 8-bit weight is its int8 codes plus one scale per output channel):
+// row-major [N][K] codes into the panel-tiled layout, codes clamped to
+// [-127, 127], padding rows and columns zero.  A wave fills one 64-byte
+// column block of 16 consecutive rows, which is 1 KiB contiguous in the tiled
+// layout (lane l: row r0 + l/4, bytes 16*(l%4) .. +15 of the block).
+__global__ __launch_bounds__(256) void k_pack_weight(const int8_t* __restrict__ src, int N, int K,
+                                                     int ldk, int vec, int8_t* __restrict__ Wq) {
+  const int lane = threadIdx.x & 63;
+  const int nblk = ldk / 64;
+  const long g = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (16-row group, block) index
+  const int rg = (int)(g / nblk), b = (int)(g % nblk);
+  const int n = rg * 16 + (lane >> 2);
+  const int k0 = b * 64 + (lane & 3) * 16;
+  if (n >= (int)padded_rows(N)) return;
+  int8_t v[16];
+  if (n < N && vec && k0 + 16 <= K) {
+    const int4 w = *reinterpret_cast<const int4*>(src + (size_t)n * K + k0);
+    __builtin_memcpy(v, &w, 16);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = (n < N && k0 + e < K) ? src[(size_t)n * K + k0 + e] : 0;
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = v[e] < -kQMax ? (int8_t)-kQMax : v[e];
+  int4 o;
+  __builtin_memcpy(&o, v, 16);
+  *reinterpret_cast<int4*>(Wq + tiled_offset(n, (size_t)k0, ldk)) = o;
+}
+
+hipError_t launch_pack_weight(const int8_t* src, int N, int K, int ldk, int8_t* Wq,
+                              hipStream_t s) {
+  const int vec = (K % 16 == 0) && ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
+  const long waves = (long)(padded_rows(N) / 16) * (ldk / 64);
+  hipLaunchKernelGGL(k_pack_weight, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, src, N, K,
+                     ldk, vec, Wq);
+  return hipGetLastError();
+}
+
 hipError_t launch_prepare_weight(const uint16_t* W, int N, int K, int ldk, int8_t* Wq,
                                  float* w_scale, hipStream_t s) {
   const int vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0);

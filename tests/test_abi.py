@@ -42,7 +42,8 @@ def test_header_declares_the_boundary():
     assert fns == sorted(["int8_weight_ld", "int8_weight_bytes", "int8_prepare_weight", "int8_matmul_workspace_size",
                           "int8_matmul", "int8_linear", "int8_matmul_stages", "int8_matmul_profiled",
                           "int8_column_absmax", "int8mm_strerror", "int8mm_last_hip_error",
-                          "int8_matmul_noalloc", "int8_matmul_noalloc_max_workspace"])
+                          "int8_matmul_noalloc", "int8_matmul_noalloc_max_workspace",
+                          "int8_pack_weight"])
     assert set(fns) == set(binding.SIGNATURES)
 
 

@@ -156,10 +156,15 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
   uint16_t* wo = out.W_O ? out.W_O : (L.decode ? nullptr : at<uint16_t>(ws, L.wo));
   // K split in the GEMM (Y output only, within the workspace's capacity):
   // its counters are zeroed by the row pass of this call
-  int nsplit = 0;
-  if (!L.decode && out.C == nullptr && out.Y != nullptr && L.nsplit > 0) {
-    nsplit = i8mm::gemm_prefill_nsplit(m, n, ldk, device_cus());
-    if (nsplit > L.nsplit) nsplit = 0;
+  int nsplit = 0, nhalf = 0;
+  if (!L.decode && out.C == nullptr && out.Y != nullptr) {
+    const int n_cu = device_cus();
+    if (L.nsplit > 0) {
+      nsplit = i8mm::gemm_prefill_nsplit(m, n, ldk, n_cu);
+      if (nsplit > L.nsplit) nsplit = 0;
+    }
+    // the last round's tiles as halves (needs no workspace)
+    if (nsplit == 0) nhalf = i8mm::gemm_prefill_nhalf(m, n, ldk, n_cu);
   }
   int32_t* ctr = nsplit ? at<int32_t>(ws, L.ctr) : nullptr;
 
@@ -199,8 +204,9 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
                                  ev_start, ev_stop);
   else
     e = i8mm::launch_gemm_prefill(xq, Wq, m, n, k, ldk, xs, w_scale, xo, wo, count, bias, Y,
-                                  out.C, nsplit, nsplit ? at<int32_t>(ws, L.cpart) : nullptr, ctr,
-                                  s, ev_start, ev_stop);
+                                  out.C, nsplit, nhalf,
+                                  nsplit ? at<int32_t>(ws, L.cpart) : nullptr, ctr, s, ev_start,
+                                  ev_stop);
   if (e != hipSuccess) return hip_fail(e);
   return INT8MM_OK;
 }

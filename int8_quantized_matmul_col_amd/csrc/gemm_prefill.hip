@@ -34,7 +34,10 @@
 // host synchronisation.
 //
 // With few tiles (at most half as many as CUs) each tile is computed by two
-// workgroups that split K and exchange int32 partials (see k_gemm_prefill).
+// workgroups that split K and exchange int32 partials.  With a last round of
+// tiles that would fill at most half of the CUs, those tiles are computed as
+// two 256x128 halves each (wave blocks of 128x64), which all run at once in
+// half the time of a whole tile (see k_gemm_prefill).
 //
 // MFMA operand convention: lane l supplies row (l%32) of its operand and 16
 // bytes of K; both fragments use the same K mapping, so the pairing of K
@@ -57,15 +60,20 @@ constexpr int NS = 4;                          // LDS stages
 constexpr int kStage = 2 * kTileBytes;         // A block then B block: 32 KiB
 constexpr int kScaleOff = NS * kStage;         // s_x[256], s_w[256], s_b[256], flag
 constexpr int kLds = kScaleOff + 3 * 1024 + 16;
-constexpr int WM = 128, WN = 128;              // wave block
-constexpr int TI = WM / 32, TJ = WN / 32;
+constexpr int WM = 128;                        // wave block rows
+constexpr int TI = WM / 32;
 constexpr int kRsrcWord3 = 0x00020000;         // raw byte buffer
+constexpr int kLoadsA = kTileBytes / 1024 / NW;  // per wave and step: 4
+// TJ (template parameter below): 32-column fragments of a wave block, 4 for a
+// whole 256x256 tile (wave block 128x128), 2 for a half tile of 256x128
+// (wave block 128x64, whose B block is the matching half of the B step block)
 
 // s_waitcnt immediate: vmcnt <= vm, lgkmcnt <= lgkm, expcnt not waited on
 constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
+template <int TJ>
 struct Frag {
   v4i a[TI];
   v4i b[TJ];
@@ -80,15 +88,18 @@ struct Pipe {
   int nk8;                    // int8 steps; steps nk8 .. last are outlier steps
   int last;                   // last pipeline step
   uint32_t goff;              // lane's byte offset in a step block for load 0
+  uint32_t boff;              // start of the B rows in a step block (half tile 1: 8 KiB)
   uint32_t ldsw;              // wave's byte offset in an operand's stage block
   uint32_t ra[2];             // fragment read offsets in a stage, sub-step kk, A
   uint32_t rb[2];             // ... B (includes the 16 KiB of the A block)
 };
 
+template <int TJ>
 __device__ __forceinline__ void make_pipe(Pipe& p, const int8_t* Xq, const int8_t* Wq,
                                           const uint16_t* XO, const uint16_t* WO, int tm, int tn,
-                                          int nk8, int k0, int n8, int n16, int wave, int lane) {
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+                                          int h, int nk8, int k0, int n8, int n16, int wave,
+                                          int lane) {
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * (32 * TJ);
   // each resource spans exactly the steps this workgroup consumes
   p.A = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const char*)Xq + ((size_t)tm * nk8 + k0) * kTileBytes), 0, n8 * kTileBytes,
@@ -110,6 +121,9 @@ __device__ __forceinline__ void make_pipe(Pipe& p, const int8_t* Xq, const int8_
   // logical chunk (s%4) ^ ((row/4)%4) (the swizzle of the fragment reads)
   const int c = (lane & 3) ^ ((lane >> 4) & 3);
   p.goff = (uint32_t)(wave * 1024 + (lane >> 2) * 64 + c * 16);
+  // B rows h*128 .. of the panel: the same swizzle (128 rows = 32 whole
+  // groups of four)
+  p.boff = (uint32_t)(h * (kTileBytes / 2));
   p.ldsw = (uint32_t)(wave * 1024);
   // fragment read of tile row r, chunk ch: slot r*4 + (ch ^ ((r/4)%4)); 16
   // consecutive rows hit 16 distinct slots of the 64 banks
@@ -129,11 +143,13 @@ struct Blk {
   uint32_t off;
 };
 __device__ __forceinline__ Blk blk(const Pipe& p, int s, bool b) {
-  if (s < p.nk8) return Blk{b ? p.B : p.A, (uint32_t)s * kTileBytes};
-  return Blk{b ? p.BO : p.AO, (uint32_t)(s - p.nk8) * kTileBytes};
+  const uint32_t o = b ? p.boff : 0u;
+  if (s < p.nk8) return Blk{b ? p.B : p.A, (uint32_t)s * kTileBytes + o};
+  return Blk{b ? p.BO : p.AO, (uint32_t)(s - p.nk8) * kTileBytes + o};
 }
 
-// Load q (0..3) of operand b of step s into stage s%NS.
+// Load q (0..3; 0..1 for the B half of a half tile) of operand b of step s
+// into stage s%NS.
 __device__ __forceinline__ void gload(char* lds, const Pipe& p, const Blk& src, int s, bool b,
                                       int q) {
   char* dst = lds + (s & (NS - 1)) * kStage + (b ? kTileBytes : 0) + q * 4096 + p.ldsw;
@@ -158,100 +174,125 @@ __device__ __forceinline__ void mma1(v16i& acc, const v4i& w, const v4i& x) {
   }
 }
 
-// Fragment read n (0..7) of sub-step kk in the order the MFMAs need them:
-// b0 a0 b1 b2 b3 a1 a2 a3 (MFMA t uses a[t/4], b[t%4]).
-__device__ __forceinline__ void fread1(Frag& f, const char* lds, uint32_t sbase, const Pipe& p,
+// Fragment read n (0 .. TI+TJ-1) of sub-step kk in the order the MFMAs need
+// them: b0 a0 b1 .. b[TJ-1] a1 .. a3 (MFMA t uses a[t/TJ], b[t%TJ]).
+template <int TJ>
+__device__ __forceinline__ void fread1(Frag<TJ>& f, const char* lds, uint32_t sbase, const Pipe& p,
                                        int kk, int n) {
-  constexpr int kind[8] = {1, 0, 1, 1, 1, 0, 0, 0};
-  constexpr int idx[8] = {0, 0, 1, 2, 3, 1, 2, 3};
-  if (kind[n])
-    f.b[idx[n]] = lread(lds, sbase + p.rb[kk] + idx[n] * 2048);
+  if (n == 0)
+    f.b[0] = lread(lds, sbase + p.rb[kk]);
+  else if (n == 1)
+    f.a[0] = lread(lds, sbase + p.ra[kk]);
+  else if (n <= TJ)
+    f.b[n - 1] = lread(lds, sbase + p.rb[kk] + (n - 1) * 2048);
   else
-    f.a[idx[n]] = lread(lds, sbase + p.ra[kk] + idx[n] * 2048);
+    f.a[n - TJ] = lread(lds, sbase + p.ra[kk] + (n - TJ) * 2048);
+}
+
+// Per step and wave: kLoadsA loads of the A block, TJ of the B block (the
+// whole 16 KiB block for TJ = 4, its half for TJ = 2).
+template <int TJ>
+constexpr int loads_per_step() {
+  return kLoadsA + TJ;
+}
+
+// The MFMA after which load q of n is issued: the loads are spread over the
+// MFMAs that follow the fragment reads.
+template <int TJ>
+constexpr int load_slot(int q, int n) {
+  return (TI + TJ) + ((q + 1) * (TI * TJ - (TI + TJ)) - 1) / n;
 }
 
 // One pipeline step kt, in a fixed instruction order (scheduling barriers
 // keep the compiler from regrouping it):
-//   phase 1: 16 MFMAs on f0 (sub-step 0 of kt); after each of the first 8 a
-//            fragment read of f1 (sub-step 1 of kt, stage kt%4); after MFMAs
-//            9, 11, 13, 15 a B load of step kt+3 into stage (kt+3)%4.
-//   wait + barrier: this wave's loads of step kt+1 have landed (the 16 loads
-//            of steps kt+2, kt+3 may still be in flight) and its fragment
-//            reads are done; after the barrier every wave's are, so stage
-//            (kt+1)%4 is complete and stage kt%4 is free.
-//   phase 2: 16 MFMAs on f1; reads of f0 (sub-step 0 of kt+1, stage
+//   phase 1: TI*TJ MFMAs on f0 (sub-step 0 of kt); after each of the first
+//            TI+TJ a fragment read of f1 (sub-step 1 of kt, stage kt%4); after
+//            the rest, the B loads of step kt+3 into stage (kt+3)%4.
+//   wait + barrier: this wave's loads of step kt+1 have landed (the loads of
+//            steps kt+2, kt+3 may still be in flight) and its fragment reads
+//            are done; after the barrier every wave's are, so stage (kt+1)%4
+//            is complete and stage kt%4 is free.
+//   phase 2: TI*TJ MFMAs on f1; reads of f0 (sub-step 0 of kt+1, stage
 //            (kt+1)%4); A loads of step kt+4 into stage kt%4.
 // Loads complete in issue order, so the loads of step j are the A half (phase
 // 2 of step j-4) then the B half (phase 1 of step j-3), and at the barrier of
-// step kt exactly 16 loads (steps kt+2, kt+3) were issued after step kt+1's.
-template <bool F16>
-__device__ __forceinline__ void step(char* lds, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
+// step kt exactly the loads of steps kt+2, kt+3 were issued after step kt+1's.
+template <bool F16, int TJ>
+__device__ __forceinline__ void step(char* lds, v16i (&acc)[TI][TJ], Frag<TJ>& f0, Frag<TJ>& f1,
                                      const Pipe& p, int kt) {
+  constexpr int MT = TI * TJ, NR = TI + TJ;
   const uint32_t cur = (uint32_t)(kt & (NS - 1)) * kStage;
   const uint32_t nxt = (uint32_t)((kt + 1) & (NS - 1)) * kStage;
   const int sb = kt + NS - 1, sa = kt + NS;
   const Blk gsb = blk(p, sb, true);
   const Blk gsa = blk(p, sa, false);
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    mma1<F16>(acc[t >> 2][t & 3], f0.b[t & 3], f0.a[t >> 2]);
+  for (int t = 0; t < MT; ++t) {
+    mma1<F16>(acc[t / TJ][t % TJ], f0.b[t % TJ], f0.a[t / TJ]);
     __builtin_amdgcn_sched_barrier(0);
-    if (t < 8) {
-      fread1(f1, lds, cur, p, 1, t);
-      __builtin_amdgcn_sched_barrier(0);
-    } else if (t & 1) {
-      gload(lds, p, gsb, sb, true, (t - 8) >> 1);
+    if (t < NR) {
+      fread1<TJ>(f1, lds, cur, p, 1, t);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int q = 0; q < TJ; ++q)
+      if (t == load_slot<TJ>(q, TJ)) {
+        gload(lds, p, gsb, sb, true, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (NS - 2), 0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * loads_per_step<TJ>(), 0));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    mma1<F16>(acc[t >> 2][t & 3], f1.b[t & 3], f1.a[t >> 2]);
+  for (int t = 0; t < MT; ++t) {
+    mma1<F16>(acc[t / TJ][t % TJ], f1.b[t % TJ], f1.a[t / TJ]);
     __builtin_amdgcn_sched_barrier(0);
-    if (t < 8) {
-      fread1(f0, lds, nxt, p, 0, t);
-      __builtin_amdgcn_sched_barrier(0);
-    } else if (t & 1) {
-      gload(lds, p, gsa, sa, false, (t - 8) >> 1);
+    if (t < NR) {
+      fread1<TJ>(f0, lds, nxt, p, 0, t);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int q = 0; q < kLoadsA; ++q)
+      if (t == load_slot<TJ>(q, kLoadsA)) {
+        gload(lds, p, gsa, sa, false, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   }
 }
 
-template <bool F16>
-__device__ __forceinline__ void run_steps(char* lds, v16i (&acc)[TI][TJ], Frag& f0, Frag& f1,
-                                          const Pipe& p, int k0, int k1) {
+template <bool F16, int TJ>
+__device__ __forceinline__ void run_steps(char* lds, v16i (&acc)[TI][TJ], Frag<TJ>& f0,
+                                          Frag<TJ>& f1, const Pipe& p, int k0, int k1) {
   int kt = k0;
   for (; kt + 2 <= k1; kt += 2) {
-    step<F16>(lds, acc, f0, f1, p, kt);
-    step<F16>(lds, acc, f0, f1, p, kt + 1);
+    step<F16, TJ>(lds, acc, f0, f1, p, kt);
+    step<F16, TJ>(lds, acc, f0, f1, p, kt + 1);
   }
-  if (kt < k1) step<F16>(lds, acc, f0, f1, p, kt);
+  if (kt < k1) step<F16, TJ>(lds, acc, f0, f1, p, kt);
 }
 
 // Pipeline prologue: loads of steps 0 .. NS-2 and the A half of step NS-1
 // (the steady state's lead), then step 0 landed everywhere and f0 holds its
 // sub-step 0.
-__device__ __forceinline__ void prologue(char* lds, Frag& f0, const Pipe& p) {
+template <int TJ>
+__device__ __forceinline__ void prologue(char* lds, Frag<TJ>& f0, const Pipe& p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const Blk a = blk(p, s, false);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) gload(lds, p, a, s, false, q);
+    for (int q = 0; q < kLoadsA; ++q) gload(lds, p, a, s, false, q);
     if (s < NS - 1) {
       const Blk b = blk(p, s, true);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) gload(lds, p, b, s, true, q);
+      for (int q = 0; q < TJ; ++q) gload(lds, p, b, s, true, q);
     }
   }
-  // issued after step 0's loads: steps 1 .. NS-2 (8 each) and A of NS-1 (4)
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (NS - 2) + 4, 0));
+  // issued after step 0's loads: steps 1 .. NS-2 and A of NS-1
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * loads_per_step<TJ>() + kLoadsA, 0));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int n = 0; n < 8; ++n) fread1(f0, lds, 0, p, 0, n);
+  for (int n = 0; n < TI + TJ; ++n) fread1<TJ>(f0, lds, 0, p, 0, n);
 }
 
 // Accumulator element r of lane `lane` for tile (i, j) holds C at row
@@ -277,11 +318,13 @@ __device__ __forceinline__ void tile_of(int b, int M, int N, int& tm, int& tn) {
   tn = (L % per_group) / gsz;
 }
 
-// Stores rows m_base .. +31, columns n_base .. +127 of Y from y (fp32,
-// accumulator layout) through the wave's 8 KiB staging area ys: each lane
-// writes its 4-column runs as 8-byte pieces (piece e of row r at position
-// e ^ 2*((r/2)%16), which spreads the rows of a write over the banks), then
-// reads back whole 16-byte pieces for 256-byte row-segment stores.
+// Stores rows m_base .. +31, columns n_base .. +32*TJ-1 of Y from y (fp32,
+// accumulator layout) through the wave's 8 KiB staging area ys (256-byte
+// rows): each lane writes its 4-column runs as 8-byte pieces (piece e of row
+// r at position e ^ 2*((r/2)%16), which spreads the rows of a write over the
+// banks), then reads back whole 16-byte pieces for row-segment stores of
+// 64*TJ bytes.
+template <int TJ>
 __device__ __forceinline__ void store_rows(const v16f (&y)[TJ], char* ys, uint16_t* __restrict__ Y,
                                            int M, int N, int m_base, int n_base, bool vec,
                                            int lane) {
@@ -300,23 +343,25 @@ __device__ __forceinline__ void store_rows(const v16f (&y)[TJ], char* ys, uint16
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int c16 = lane & 15;
-  const int n_col = n_base + c16 * 8;
+  constexpr int PR = 4 * TJ;   // 16-byte pieces of a row segment
+  constexpr int RPP = 64 / PR;  // rows per pass
+  const int c = lane % PR;
+  const int n_col = n_base + c * 8;
 #pragma unroll
-  for (int pp = 0; pp < 8; ++pp) {
-    const int rl = pp * 4 + (lane >> 4);
+  for (int pp = 0; pp < 32 / RPP; ++pp) {
+    const int rl = pp * RPP + lane / PR;
     const int m = m_base + rl;
-    const int pos = (2 * c16) ^ (2 * ((rl >> 1) & 15));  // even: the pair stays in order
+    const int pos = (2 * c) ^ (2 * ((rl >> 1) & 15));  // even: the pair stays in order
     const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 256 + pos * 8);
     if (m < M) {
       if (vec && n_col + 8 <= N) {
         // Y is written once and not read again here: stream it past the caches
         __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col));
       } else {
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+        const uint16_t* hh = reinterpret_cast<const uint16_t*>(&v);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (n_col + e < N) Y[(size_t)m * N + n_col + e] = h[e];
+          if (n_col + e < N) Y[(size_t)m * N + n_col + e] = hh[e];
       }
     }
   }
@@ -338,7 +383,8 @@ __device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restri
                                                uint16_t* __restrict__ Y, int tm, int tn) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  constexpr int TJ = 4;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * (32 * TJ);
   const int m0 = tm * BM, n0 = tn * BN;
   const float* s_x = reinterpret_cast<const float*>(lds + kScaleOff);
   const float* s_w = s_x + BM;
@@ -347,15 +393,15 @@ __device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restri
   const int nk16 = (n_out + 31) / 32;
   const int n8 = n_out < K ? nk8 : 0;
   Pipe p;
-  make_pipe(p, Xq, Wq, XO, WO, tm, tn, nk8, 0, n8, nk16, wave, lane);
+  make_pipe<TJ>(p, Xq, Wq, XO, WO, tm, tn, 0, nk8, 0, n8, nk16, wave, lane);
   v16i acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
-  Frag f0, f1;
+  Frag<TJ> f0, f1;
   prologue(lds, f0, p);
-  run_steps<false>(lds, acc, f0, f1, p, 0, n8);
+  run_steps<false, TJ>(lds, acc, f0, f1, p, 0, n8);
   // one column quad at a time (its scales and biases read once, applied to
   // the four row groups), so that few registers are live beside the
   // accumulators
@@ -377,7 +423,7 @@ __device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restri
               __float_as_int((float)acc[i][j][4 * q + e] * (sx[i] * w4[e]) + b4[e]);
       __builtin_amdgcn_sched_barrier(0);
     }
-  run_steps<true>(lds, acc, f0, f1, p, n8, n8 + nk16);
+  run_steps<true, TJ>(lds, acc, f0, f1, p, n8, n8 + nk16);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const bool vec = (N & 7) == 0;
@@ -387,73 +433,38 @@ __device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restri
     v16f y[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) y[j] = __builtin_bit_cast(v16f, acc[i][j]);
-    store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
+    store_rows<TJ>(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
   }
 }
 
-}  // namespace
-
-// nsplit (MODE 0 only): the last nsplit tiles (in workgroup order) are each
-// computed by two workgroups, unit u = 0 .. nsplit-1 as workgroups
-// nwhole + u (half 0: int8 steps [0, nk8/2)) and nwhole + nsplit + u (half 1:
-// [nk8/2, nk8)), after the nwhole = tiles - nsplit whole tiles.  Each half
-// stores its int32 partial in cpart; the second to finish (counter ctr[u],
-// zeroed by the activation pass of the same call) adds the other's partial,
-// an exact integer sum, and runs the epilogue.  Used when the tiles would
-// leave most of the GPU idle.
-template <int MODE>  // 0: Y (fused epilogue), 1: int32 C
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
-k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
-               int ldk, const float* __restrict__ x_scale, const float* __restrict__ w_scale,
-               const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
-               const int32_t* __restrict__ n_out, const uint16_t* __restrict__ bias,
-               uint16_t* __restrict__ Y, int32_t* __restrict__ C, int nsplit,
-               int32_t* __restrict__ cpart, int32_t* __restrict__ ctr) {
-  __shared__ __attribute__((aligned(1024))) char lds[kLds];
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int nwhole = tiles - nsplit;
-  int tb = (int)blockIdx.x, half = 0, su = -1;  // su: split unit of this workgroup
-  if ((int)blockIdx.x >= nwhole) {
-    const int bb = (int)blockIdx.x - nwhole;
-    su = bb % nsplit;
-    half = bb / nsplit;
-    tb = nwhole + su;
-  }
-  const bool split = su >= 0;
+// The tile's work after the scales are staged: the int8 pipeline, then the
+// K-split exchange (SPLIT: whole tiles in MODE 0 only), then the C store
+// (MODE 1) or the fused epilogue.  TJ = 4: the whole tile (n0 = its first
+// column); TJ = 2: the half tile h, columns n0 = tile start + 128h on.
+template <int MODE, int TJ, bool SPLIT>
+__device__ __forceinline__ void tile_work(char* lds, const int8_t* __restrict__ Xq,
+                                          const int8_t* __restrict__ Wq, int M, int N, int nk8,
+                                          int nk16, const uint16_t* __restrict__ XO,
+                                          const uint16_t* __restrict__ WO,
+                                          uint16_t* __restrict__ Y, int32_t* __restrict__ C,
+                                          int tm, int tn, int h, int m0, int n0, int su, int half,
+                                          int32_t* __restrict__ cpart, int32_t* __restrict__ ctr) {
+  static_assert(!SPLIT || (MODE == 0 && TJ == 4), "K split: whole tiles, Y output");
+  const bool split = SPLIT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-  int tm, tn;
-  tile_of(tb, M, N, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * (32 * TJ);
+  const float* s_x = reinterpret_cast<const float*>(lds + kScaleOff);
+  const float* s_w = s_x + BM;
+  const float* s_b = s_w + BN;
+  int* s_flag = reinterpret_cast<int*>(lds + kScaleOff + 3 * 1024);
 
-  // the tile's scales (w_scale already divided by 127^2) and biases, read by
-  // the epilogue after the loop's barriers have published them
-  float* s_x = reinterpret_cast<float*>(lds + kScaleOff);
-  float* s_w = s_x + BM;
-  float* s_b = s_w + BN;
-  int* s_flag = reinterpret_cast<int*>(s_b + BN);
-  if (MODE == 0) {
-    const int t = threadIdx.x;
-    s_x[t] = x_scale[min(m0 + t, M - 1)];
-    s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
-    s_b[t] = bias != nullptr ? h2f(bias[min(n0 + t, N - 1)]) : 0.0f;
-  }
-
-  const int nk8 = ldk / kTileK;
-  const int nk16 = MODE == 0 ? (*n_out + 31) / 32 : 0;
-  if (MODE == 0 && nk16 > NS - 1) {
-    // whole tile in one workgroup (half 0 of a split unit is workgroup tb)
-    __syncthreads();  // the tile's scales are in LDS
-    if (half == 0) gemm_tile_many(lds, Xq, Wq, M, N, K, ldk, XO, WO, *n_out, Y, tm, tn);
-    return;
-  }
   // this workgroup's int8 steps [k0, k0 + nr); pipeline step s < nr is int8
   // step k0 + s, then come the outlier steps
-  const int k0 = half ? nk8 / 2 : 0;
+  const int k0 = split && half ? nk8 / 2 : 0;
   const int nr = split ? (half ? nk8 - nk8 / 2 : nk8 / 2) : nk8;
   Pipe p;
-  make_pipe(p, Xq, Wq, XO, WO, tm, tn, nk8, k0, nr, nk16, wave, lane);
+  make_pipe<TJ>(p, Xq, Wq, XO, WO, tm, tn, h, nk8, k0, nr, nk16, wave, lane);
 
   v16i acc[TI][TJ];
 #pragma unroll
@@ -461,65 +472,41 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16i{};
 
-  Frag f0, f1;
-  prologue(lds, f0, p);
+  Frag<TJ> f0, f1;
+  prologue<TJ>(lds, f0, p);
   // int8 x int8 -> int32 over this workgroup's K steps (outlier columns of
   // Xq are zero); the loads of the outlier steps ride along
-  run_steps<false>(lds, acc, f0, f1, p, 0, nr);
+  run_steps<false, TJ>(lds, acc, f0, f1, p, 0, nr);
 
-  if (MODE == 0 && split) {
-    // partial of this half, four registers per pass: each lane stores 16
-    // bytes, each wave 1 KiB contiguous
-    constexpr int kQuads = TI * TJ * 4;
-    v4i* mine =
-        reinterpret_cast<v4i*>(cpart) + ((size_t)su * 2 + half) * kQuads * NT + threadIdx.x;
-    const v4i* other =
-        reinterpret_cast<const v4i*>(cpart) + ((size_t)su * 2 + (half ^ 1)) * kQuads * NT +
-        threadIdx.x;
+  if constexpr (SPLIT) {
+    {
+      // partial of this half, four registers per pass: each lane stores 16
+      // bytes, each wave 1 KiB contiguous
+      constexpr int kQuads = TI * TJ * 4;
+      v4i* mine =
+          reinterpret_cast<v4i*>(cpart) + ((size_t)su * 2 + half) * kQuads * NT + threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          mine[((i * TJ + j) * 4 + q) * NT] =
-              v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores (and every load) have landed
-    __syncthreads();                // ... and every other thread's
-    if (threadIdx.x == 0) {
-      __threadfence();  // the partial is visible device-wide before the count
-      const int first = atomicAdd(&ctr[su], 1) == 0;
-      if (!first) __threadfence();  // and the other half's is seen after it
-      *s_flag = first;
-    }
-    __syncthreads();
-    if (*s_flag) return;  // the other half finishes the tile
-    // the other half's partial in two batches of 32 loads per lane, each
-    // batch entirely in flight before its adds (one memory round trip per
-    // batch, not per load)
-#pragma unroll
-    for (int i0 = 0; i0 < TI; i0 += 2) {
-      v4i o[2][TJ][4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) o[i][j][q] = other[(((i0 + i) * TJ + j) * 4 + q) * NT];
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i0 + i][j][4 * q + e] += o[i][j][q][e];
-      __builtin_amdgcn_sched_barrier(0);
+            mine[((i * TJ + j) * 4 + q) * NT] = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                    acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      __builtin_amdgcn_s_waitcnt(0);  // this thread's stores (and every load) have landed
+      __syncthreads();                // ... and every other thread's
+      if (threadIdx.x == 0) {
+        __threadfence();  // the partial is visible device-wide before the count
+        const int first = atomicAdd(&ctr[su], 1) == 0;
+        if (!first) __threadfence();  // and the other half's is seen after it
+        *s_flag = first;
+      }
+      __syncthreads();
+      if (*s_flag) return;  // the other half finishes the tile
     }
   }
 
-  if (MODE == 1) {
+  if constexpr (MODE == 1) {
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -544,15 +531,51 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   __syncthreads();
   const bool vec = (N & 7) == 0;
   char* ys = lds + ((nr + NS - 1) & (NS - 1)) * kStage + wave * 8192;
+  // K split: the other half's int32 partial, added per row group (an exact
+  // integer sum) as it is converted; group i+1's loads are in flight while
+  // group i is finished and stored
+  v4i onext[SPLIT ? TJ : 1][4];
+  const v4i* other = nullptr;
+  if constexpr (SPLIT) {
+    other = reinterpret_cast<const v4i*>(cpart) +
+            ((size_t)su * 2 + (half ^ 1)) * (TI * TJ * 4) * NT + threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) onext[j][q] = other[(j * 4 + q) * NT];
+  }
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
+    if constexpr (SPLIT) {
+      v4i ocur[TJ][4];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ocur[j][q] = onext[j][q];
+      if (i + 1 < TI) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) onext[j][q] = other[(((i + 1) * TJ + j) * 4 + q) * NT];
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += ocur[j][q][e];
+    }
     const float sx = s_x[wm0 + i * 32 + (lane & 31)];
+    // the column scales and biases are read again for every row group: held
+    // across the groups they would take 32*TJ registers and force spills
+    int cb = wn0 + (lane >> 5) * 4;
+    asm volatile("" : "+v"(cb));
     v16f y[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int c = wn0 + j * 32 + q * 8 + (lane >> 5) * 4;
+        const int c = cb + j * 32 + q * 8;
         const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[c]);
         const v4f b4 = *reinterpret_cast<const v4f*>(&s_b[c]);
 #pragma unroll
@@ -571,24 +594,123 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
         }
       }
     }
-    store_rows(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
+    store_rows<TJ>(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
+  }
+}
+
+}  // namespace
+
+// SPLIT = false: workgroups 0 .. nwhole-1 compute whole tiles (in workgroup
+// order), then come nhalf half-tile pairs (MODE 0 only): each of the last
+// nhalf tiles is computed as two 256x128 halves by two workgroups 8 apart (so
+// on the same XCD, sharing the A panel in its L2).  Used when the last round
+// of whole tiles would fill at most half of the CUs: its halves then all run
+// at once, in half the time.
+// SPLIT = true (MODE 0): every tile u is computed by two workgroups, u (half
+// 0: int8 steps [0, nk8/2)) and tiles + u (half 1: [nk8/2, nk8)).  Each half
+// stores its int32 partial in cpart; the second to finish (counter ctr[u],
+// zeroed by the activation pass of the same call) adds the other's partial,
+// an exact integer sum, and runs the epilogue.  Used when the tiles would
+// leave most of the GPU idle.  A kernel of its own, so that the registers its
+// exchange needs do not weigh on the whole-tile code.
+template <int MODE, bool SPLIT>  // MODE 0: Y (fused epilogue), 1: int32 C
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
+k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
+               int ldk, const float* __restrict__ x_scale, const float* __restrict__ w_scale,
+               const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
+               const int32_t* __restrict__ n_out, const uint16_t* __restrict__ bias,
+               uint16_t* __restrict__ Y, int32_t* __restrict__ C, int nhalf,
+               int32_t* __restrict__ cpart, int32_t* __restrict__ ctr) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLds];
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  // su: split unit of this workgroup; ht: a half tile, `half` its column half
+  int tb = (int)blockIdx.x, half = 0, su = -1;
+  bool ht = false;
+  if constexpr (SPLIT) {
+    su = tb % tiles;
+    half = tb / tiles;
+    tb = su;
+  } else {
+    const int nwhole = tiles - nhalf;
+    if (tb >= nwhole) {
+      // groups of 8 tiles: workgroups bb and bb + 8 of a group of 16 take the
+      // two halves of one tile; the last nhalf % 8 tiles in adjacent pairs
+      const int bb = tb - nwhole;
+      const int g16 = 16 * (nhalf / 8);
+      int t;
+      if (bb < g16) {
+        t = (bb / 16) * 8 + bb % 8;
+        half = (bb / 8) & 1;
+      } else {
+        t = 8 * (nhalf / 8) + (bb - g16) / 2;
+        half = (bb - g16) & 1;
+      }
+      tb = nwhole + t;
+      ht = true;
+    }
+  }
+  int tm, tn;
+  tile_of(tb, M, N, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN + (ht ? half * (BN / 2) : 0);
+
+  // the unit's scales (w_scale already divided by 127^2) and biases, read by
+  // the epilogue after the loop's barriers have published them
+  float* s_x = reinterpret_cast<float*>(lds + kScaleOff);
+  float* s_w = s_x + BM;
+  float* s_b = s_w + BN;
+  if (MODE == 0) {
+    const int t = threadIdx.x;
+    s_x[t] = x_scale[min(m0 + t, M - 1)];
+    s_w[t] = w_scale[min(n0 + t, N - 1)] * kInv127Sq;
+    s_b[t] = bias != nullptr ? h2f(bias[min(n0 + t, N - 1)]) : 0.0f;
+  }
+
+  const int nk8 = ldk / kTileK;
+  const int nk16 = MODE == 0 ? (*n_out + 31) / 32 : 0;
+  if (MODE == 0 && nk16 > NS - 1) {
+    // whole tile in one workgroup: half 0 of a split unit or of a half-tile
+    // pair (its scales start at the tile's first column) computes it
+    __syncthreads();  // the tile's scales are in LDS
+    if (half == 0) gemm_tile_many(lds, Xq, Wq, M, N, K, ldk, XO, WO, *n_out, Y, tm, tn);
+    return;
+  }
+  if constexpr (SPLIT) {
+    tile_work<MODE, 4, true>(lds, Xq, Wq, M, N, nk8, nk16, XO, WO, Y, C, tm, tn, 0, m0, n0, su,
+                             half, cpart, ctr);
+  } else {
+    if constexpr (MODE == 0) {
+      if (ht) {
+        tile_work<MODE, 2, false>(lds, Xq, Wq, M, N, nk8, nk16, XO, WO, Y, C, tm, tn, half, m0,
+                                  n0, -1, 0, cpart, ctr);
+        return;
+      }
+    }
+    tile_work<MODE, 4, false>(lds, Xq, Wq, M, N, nk8, nk16, XO, WO, Y, C, tm, tn, 0, m0, n0, -1,
+                              0, cpart, ctr);
   }
 }
 
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, const uint16_t* bias,
-                               uint16_t* Y, int32_t* C, int nsplit, int32_t* cpart, int32_t* ctr,
-                               hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                               uint16_t* Y, int32_t* C, int nsplit, int nhalf, int32_t* cpart,
+                               int32_t* ctr, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  // a K split covers every tile; half tiles, a tail of at most all of them
+  if ((nsplit != 0 && nsplit != tiles) || nhalf < 0 || nhalf > tiles || (nsplit > 0 && nhalf > 0))
+    return hipErrorInvalidValue;
   if (C != nullptr)
-    hipExtLaunchKernelGGL(k_gemm_prefill<1>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
-                          K, ldk, x_scale, w_scale, XO, WO, n_out, nullptr, Y, C, 0, nullptr,
-                          nullptr);
+    hipExtLaunchKernelGGL((k_gemm_prefill<1, false>), dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq,
+                          Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, nullptr, Y, C, 0,
+                          nullptr, nullptr);
+  else if (nsplit > 0)
+    hipExtLaunchKernelGGL((k_gemm_prefill<0, true>), dim3(2 * tiles), dim3(NT), 0, s, e0, e1, 0,
+                          Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, bias, Y, C, 0,
+                          cpart, ctr);
   else
-    hipExtLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles + nsplit), dim3(NT), 0, s, e0, e1, 0,
-                          Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, bias, Y, C,
-                          nsplit, cpart, ctr);
+    hipExtLaunchKernelGGL((k_gemm_prefill<0, false>), dim3(tiles + nhalf), dim3(NT), 0, s, e0, e1,
+                          0, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, bias, Y, C,
+                          nhalf, cpart, ctr);
   return hipGetLastError();
 }
 
@@ -600,6 +722,15 @@ int gemm_prefill_nsplit(int M, int N, int ldk, int n_cu) {
   // round measured no faster: the exchange of the int32 partials (HBM-bound
   // when all the split units end together) costs about what it saves.
   return 2 * tiles <= n_cu ? tiles : 0;
+}
+
+int gemm_prefill_nhalf(int M, int N, int ldk, int n_cu) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (n_cu <= 0 || gemm_prefill_nsplit(M, N, ldk, n_cu) > 0) return 0;
+  // one workgroup per CU: the tiles of a last round that fills at most half
+  // of the CUs run as halves, all at once
+  const int tail = tiles % n_cu;
+  return tiles >= n_cu && 2 * tail <= n_cu ? tail : 0;
 }
 
 }  // namespace i8mm

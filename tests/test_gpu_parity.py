@@ -57,6 +57,12 @@ SHAPES = [
     (300, 2112, 520, 7, 6.0),      # K split over two workgroups per tile, odd step count
     (260, 2048, 300, 2, 0.0),      # split grid with every column an outlier
     (300, 9000, 64, 5, 6.0),       # rows too long for one wave: a block per row
+    # more tiles than CUs with a short last round: its 14 tiles run as
+    # 256x128 halves (one group of 8 pairs, 6 adjacent pairs), ragged in M
+    # and N; then the same with more than three fp16 outlier steps (the
+    # first half of each pair computes the whole tile)
+    (2200, 96, 7600, 3, 6.0),
+    (2200, 256, 7600, 100, 6.0),
 ]
 
 

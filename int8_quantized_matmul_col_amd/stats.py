@@ -9,8 +9,11 @@ too high a one quantizes the outliers (accuracy collapses).
 
 What decides the split is the per-column maximum colmax[k] = max_m |X[m,k]|:
 column k is an outlier column for every threshold t < colmax[k].  It comes
-from the library's outlier-detection kernels (``int8_column_absmax``); the
-summaries below are small reductions over those K values.
+from the library's outlier-detection kernels (``int8_column_absmax``, exact).
+The summaries below are tool logic, not a step of the matmul path: small
+torch reductions over those K values (counts of colmax > t, a percentile)
+that report what each candidate threshold would send to fp16.  The path's
+own comparison with the threshold is done inside the library's kernels.
 """
 
 from __future__ import annotations

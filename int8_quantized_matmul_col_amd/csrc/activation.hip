@@ -477,7 +477,7 @@ constexpr int kWoRows = 16;
 constexpr int kRowBlocks = 2048;  // row blocks of the one-wave-per-row form
 
 template <int WPR, int CPL>
-__global__ __launch_bounds__(256) void k_quant_rows(
+__device__ __forceinline__ void quant_rows_body(
     const uint16_t* __restrict__ X, int M, int K, int ldk, int vec, int n_wo_blocks,
     const uint32_t* __restrict__ mask_bits, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
     uint16_t* __restrict__ XO, int32_t* __restrict__ n_out, int32_t* __restrict__ out_idx,
@@ -588,6 +588,28 @@ __global__ __launch_bounds__(256) void k_quant_rows(
                             x_scale, XO);
   }
 }
+
+#define I8MM_QUANT_ROWS_ARGS                                                                   \
+  const uint16_t *__restrict__ X, int M, int K, int ldk, int vec, int n_wo_blocks,              \
+      const uint32_t *__restrict__ mask_bits, int8_t *__restrict__ Xq,                          \
+      float *__restrict__ x_scale, uint16_t *__restrict__ XO, int32_t *__restrict__ n_out,     \
+      int32_t *__restrict__ out_idx, const int8_t *__restrict__ Wq,                             \
+      const float *__restrict__ w_scale, int N, uint16_t *__restrict__ WO,                      \
+      int32_t *__restrict__ zero_ctr, int n_zero
+template <int WPR, int CPL>
+__global__ __launch_bounds__(256) void k_quant_rows(I8MM_QUANT_ROWS_ARGS) {
+  quant_rows_body<WPR, CPL>(X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out,
+                            out_idx, Wq, w_scale, N, WO, zero_ctr, n_zero);
+}
+// The same held to 128 registers (4 waves per SIMD: a wave per row for 16
+// rows per CU at once)
+template <int WPR, int CPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_quant_rows4(
+    I8MM_QUANT_ROWS_ARGS) {
+  quant_rows_body<WPR, CPL>(X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out,
+                            out_idx, Wq, w_scale, N, WO, zero_ctr, n_zero);
+}
+#undef I8MM_QUANT_ROWS_ARGS
 
 // ---------------------------------------------------------------- few rows
 
@@ -738,8 +760,12 @@ static void launch_qr(dim3 grid, size_t lds, hipStream_t s, const uint16_t* X, i
                       int ldk, int vec, int nwb, const uint32_t* mb, int8_t* Xq, float* xs,
                       uint16_t* XO, int32_t* n_out, int32_t* out_idx, const int8_t* Wq,
                       const float* ws, int N, uint16_t* WO, int32_t* zc, int nz) {
-  hipLaunchKernelGGL((k_quant_rows<WPR, CPL>), grid, dim3(256), lds, s, X, M, K, ldk, vec, nwb, mb,
-                     Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO, zc, nz);
+  if (WPR == 1 && CPL == 10)
+    hipLaunchKernelGGL((k_quant_rows4<WPR, CPL>), grid, dim3(256), lds, s, X, M, K, ldk, vec, nwb,
+                       mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO, zc, nz);
+  else
+    hipLaunchKernelGGL((k_quant_rows<WPR, CPL>), grid, dim3(256), lds, s, X, M, K, ldk, vec, nwb,
+                       mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO, zc, nz);
 }
 
 hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uint32_t* mask_bits,
@@ -766,13 +792,17 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
   if (!vec) {
     if (wpr == 4) QR(4, 0); else QR(1, 0);
   } else if (wpr == 4) {
+    // (register forms sized to the row: every chunk slot held is quantized)
     if (cpl_needed <= 4) QR(4, 4);
+    else if (cpl_needed <= 6) QR(4, 6);
     else if (cpl_needed <= 8) QR(4, 8);
     else QR(4, 0);
   } else {
     if (cpl_needed <= 2) QR(1, 2);
     else if (cpl_needed <= 4) QR(1, 4);
+    else if (cpl_needed <= 6) QR(1, 6);
     else if (cpl_needed <= 8) QR(1, 8);
+    else if (cpl_needed <= 10) QR(1, 10);
     else if (cpl_needed <= 12) QR(1, 12);
     else if (cpl_needed <= 16) QR(1, 16);
     else QR(1, 0);

@@ -122,25 +122,30 @@ __device__ __forceinline__ uint2 pack8_i8(const int (&q)[8]) {
 
 // Codes of the 8 columns of a chunk against the row scale a, with
 // r = RN(127/a) (0 when a == 0).  For |x| <= a the exact product x*r lies
-// within 2^-17 of the exact 127x/a, so t = rint(RN(x*r)) is the exact
-// round-half-even code wherever |x*r - t| (one fma) is at most 1/2 - 2^-14;
-// there it also equals rint of the IEEE quotient fp32(127x)/a (checked on
-// every binary16 pair 0 <= x <= a on the host).  Returns the largest such
-// deviation in *dev: above kTieGuard (about 1.5e-4 of the values) the caller
-// recomputes the chunk with quant8_exact.  Outlier columns (|x| > a) get
-// arbitrary codes here; the caller zeroes them.  Branch-free, so the chunks
-// of a row interleave.
+// within 2^-17 of the exact 127x/a.  One fma adds 1.5*2^23 to it: the fp32
+// sum has unit spacing, so it holds t = the exact product rounded half-even
+// to an integer, and its low byte is t's two's-complement code (|t| <= 127;
+// no conversion instruction).  t is the exact round-half-even code wherever
+// |x*r - t| (one fma) is at most 1/2 - 2^-14; there it also equals rint of
+// the IEEE quotient fp32(127x)/a (checked on every binary16 pair
+// 0 <= x <= a on the host).  Returns the largest such deviation in *dev:
+// above kTieGuard (about 1.5e-4 of the values) the caller recomputes the
+// chunk with quant8_exact.  Outlier columns (|x| > a) get arbitrary codes
+// here; the caller zeroes them.  Branch-free, so the chunks of a row
+// interleave.
 __device__ __forceinline__ uint2 quant8_fast(const uint4& w, float r, float* dev) {
+  constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
   int q[8];
   float d = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float x = h2f((uint16_t)half_at(w, i));
-    // RN(x*r) as an fma with a +0 addend, so it reads the binary16 operand
-    // directly (a -0 product becomes +0, which quantizes the same)
-    const float t = rintf(__builtin_fmaf(x, r, 0.0f));
+    // fma reading the binary16 operand directly; exact integer t after the
+    // subtraction (|x*r| < 2^22 on the regular columns)
+    const float s = __builtin_fmaf(x, r, kRound);
+    const float t = s - kRound;
     d = fmaxf(d, fabsf(__builtin_fmaf(x, r, -t)));
-    q[i] = (int)t;
+    q[i] = (int)__float_as_uint(s);  // low byte: the code
   }
   *dev = d;
   return pack8_i8(q);

@@ -57,6 +57,9 @@ SHAPES = [
     (300, 2112, 520, 7, 6.0),      # K split over two workgroups per tile, odd step count
     (260, 2048, 300, 2, 0.0),      # split grid with every column an outlier
     (300, 9000, 64, 5, 6.0),       # rows too long for one wave: a block per row
+    (300, 4700, 64, 5, 6.0),       # row pass held in 10 chunks per lane (4 waves per SIMD)
+    (280, 2600, 64, 3, 6.0),       # ... 6 chunks per lane
+    (40, 10000, 64, 3, 6.0),       # a block per row, 6 chunks per lane
     # more tiles than CUs with a short last round: its 14 tiles run as
     # 256x128 halves (one group of 8 pairs, 6 adjacent pairs), ragged in M
     # and N; then the same with more than three fp16 outlier steps (the

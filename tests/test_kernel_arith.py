@@ -1,8 +1,9 @@
 """Host checks of arithmetic shortcuts taken by the HIP kernels.
 
-The activation kernel quantizes a row with r = RN(127/a) and t = rint(RN(x*r)),
-and falls back to the IEEE division fp32(127*x)/a wherever |x*r - t| (one
-fused multiply-add, rounded once to fp32) exceeds 1/2 - 2^-14.  The test below
+The activation kernel quantizes a row with r = RN(127/a) and t = the exact
+product x*r rounded half-even to an integer (one fma adding 1.5*2^23), and
+falls back to the IEEE division fp32(127*x)/a wherever |x*r - t| (one fused
+multiply-add, rounded once to fp32) exceeds 1/2 - 2^-14.  The test below
 runs that rule, in numpy float32 / float64, over every binary16 pair
 0 <= x <= a (a > 0 finite, about 5e8 pairs) and checks that where the kernel
 keeps t it equals rint(fp32(fp32(127*x)/a)), the quantizer that defines the
@@ -25,7 +26,8 @@ def test_fast_quantizer_matches_ieee_division_on_all_binary16_pairs():
         a = allf[ia]
         x = allf[: ia + 1]
         r = np.float32(127.0) / a                       # correctly rounded fp32 division
-        t = np.rint(x * r)                              # RN product, then half-even
+        # exact product (24 + 11 significant bits fit float64), half-even integer
+        t = np.rint(x.astype(np.float64) * np.float64(r))
         # fma(x, r, -t): exact in float64 (24 + 11 significant bits), then one fp32 rounding
         dev = np.abs((x.astype(np.float64) * np.float64(r) - t).astype(np.float32))
         keep = dev <= GUARD

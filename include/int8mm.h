@@ -35,9 +35,9 @@
  *     different workspaces may run concurrently.  Two calls that share a
  *     workspace must be ordered (e.g. on one stream).
  *   - A call can be captured in a HIP graph and replayed: it records only
- *     kernel launches (counters and fills are cleared by kernels, never by
- *     hipMemsetAsync), and every counter it relies on is cleared by an
- *     earlier kernel of the same call.
+ *     kernel launches (fills are done by kernels, never by hipMemsetAsync),
+ *     and every workspace region a kernel reads was written by an earlier
+ *     kernel of the same call (no counters are kept between calls).
  *   - X and Y are row-major.  The int8 operands and the fp16 outlier slices
  *     (the prepared weight Wq, and the stage outputs Xq, X_O, W_O) use the
  *     library's panel-tiled layout, built for gfx950's memory path: rows are
@@ -263,8 +263,8 @@ INT8MM_API int int8_matmul_profiled(const int8mm_half* X, int64_t M, int64_t K,
  *                    X + outlier slices).
  * Every call on one GPU uses that GPU's single buffer, which keeps the last
  * call's contents: calls that overlap on one GPU (concurrent streams, or
- * host threads) race and must be ordered by the caller.  Every counter the
- * kernels rely on is cleared by an earlier kernel of the same call.
+ * host threads) race and must be ordered by the caller.  Every part of it
+ * that a kernel reads was written by an earlier kernel of the same call.
  */
 #define INT8MM_NOALLOC_SCRATCH_BYTES (64u << 20)
 

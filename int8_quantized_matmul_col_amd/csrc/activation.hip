@@ -482,7 +482,7 @@ __device__ __forceinline__ void quant_rows_body(
     const uint32_t* __restrict__ mask_bits, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
     uint16_t* __restrict__ XO, int32_t* __restrict__ n_out, int32_t* __restrict__ out_idx,
     const int8_t* __restrict__ Wq, const float* __restrict__ w_scale, int N,
-    uint16_t* __restrict__ WO, int32_t* __restrict__ zero_ctr, int n_zero) {
+    uint16_t* __restrict__ WO) {
   extern __shared__ uint32_t s_dyn[];
   __shared__ uint32_t s_red[4];
   const int nw = ldk / 32;
@@ -521,8 +521,6 @@ __device__ __forceinline__ void quant_rows_body(
   __syncthreads();
 
   if (rb == 0) {
-    // counters the GEMM of this call starts from zero
-    for (int i = t; i < n_zero; i += 256) zero_ctr[i] = 0;
     if (t == 0 && n_out != nullptr) *n_out = total;
     if (out_idx != nullptr) {
       for (int w = t; w < nw; w += 256) {
@@ -594,12 +592,11 @@ __device__ __forceinline__ void quant_rows_body(
       const uint32_t *__restrict__ mask_bits, int8_t *__restrict__ Xq,                          \
       float *__restrict__ x_scale, uint16_t *__restrict__ XO, int32_t *__restrict__ n_out,     \
       int32_t *__restrict__ out_idx, const int8_t *__restrict__ Wq,                             \
-      const float *__restrict__ w_scale, int N, uint16_t *__restrict__ WO,                      \
-      int32_t *__restrict__ zero_ctr, int n_zero
+      const float *__restrict__ w_scale, int N, uint16_t *__restrict__ WO
 template <int WPR, int CPL>
 __global__ __launch_bounds__(256) void k_quant_rows(I8MM_QUANT_ROWS_ARGS) {
   quant_rows_body<WPR, CPL>(X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out,
-                            out_idx, Wq, w_scale, N, WO, zero_ctr, n_zero);
+                            out_idx, Wq, w_scale, N, WO);
 }
 // The same held to 128 registers (4 waves per SIMD: a wave per row for 16
 // rows per CU at once)
@@ -607,7 +604,7 @@ template <int WPR, int CPL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_quant_rows4(
     I8MM_QUANT_ROWS_ARGS) {
   quant_rows_body<WPR, CPL>(X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out,
-                            out_idx, Wq, w_scale, N, WO, zero_ctr, n_zero);
+                            out_idx, Wq, w_scale, N, WO);
 }
 #undef I8MM_QUANT_ROWS_ARGS
 
@@ -759,19 +756,19 @@ template <int WPR, int CPL>
 static void launch_qr(dim3 grid, size_t lds, hipStream_t s, const uint16_t* X, int M, int K,
                       int ldk, int vec, int nwb, const uint32_t* mb, int8_t* Xq, float* xs,
                       uint16_t* XO, int32_t* n_out, int32_t* out_idx, const int8_t* Wq,
-                      const float* ws, int N, uint16_t* WO, int32_t* zc, int nz) {
+                      const float* ws, int N, uint16_t* WO) {
   if (WPR == 1 && CPL == 10)
     hipLaunchKernelGGL((k_quant_rows4<WPR, CPL>), grid, dim3(256), lds, s, X, M, K, ldk, vec, nwb,
-                       mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO, zc, nz);
+                       mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO);
   else
     hipLaunchKernelGGL((k_quant_rows<WPR, CPL>), grid, dim3(256), lds, s, X, M, K, ldk, vec, nwb,
-                       mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO, zc, nz);
+                       mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO);
 }
 
 hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uint32_t* mask_bits,
                              int8_t* Xq, float* x_scale, uint16_t* XO, int32_t* n_out,
                              int32_t* out_idx, const int8_t* Wq, const float* w_scale, int N,
-                             uint16_t* WO, int32_t* zero_ctr, int n_zero, hipStream_t s) {
+                             uint16_t* WO, hipStream_t s) {
   const int vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
   // a whole block per row for few rows (keeps the GPU busy) and for rows too
   // long for one wave's registers but not for four waves' (so the row is
@@ -787,7 +784,7 @@ hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uin
   dim3 grid(n_row_blocks + n_wo_blocks);
   const int lanes = 64 * wpr;
   const int cpl_needed = (ldk / 8 + lanes - 1) / lanes;
-#define QR(W, C) launch_qr<W, C>(grid, lds, s, X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out, out_idx, Wq, w_scale, N, WO, zero_ctr, n_zero)
+#define QR(W, C) launch_qr<W, C>(grid, lds, s, X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out, out_idx, Wq, w_scale, N, WO)
   // rows held in registers need 16-byte loads (aligned X, K % 8 == 0)
   if (!vec) {
     if (wpr == 4) QR(4, 0); else QR(1, 0);

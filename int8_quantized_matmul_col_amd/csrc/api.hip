@@ -22,7 +22,6 @@ int hip_fail(hipError_t e) {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kLayoutCUs = 256;  // MI355X compute units
 
 // Compute units of the current device (cached per device).
 int device_cus() {
@@ -48,8 +47,6 @@ struct Layout {
   bool decode = false;
   int rc = 0;  // row chunks of the column-absmax pass (prefill path)
   size_t part = 0, bits = 0, count = 0, xscale = 0, xq = 0, xo = 0, wo = 0, total = 0;
-  int nsplit = 0;  // prefill GEMM tiles computed by two workgroups (K split)
-  size_t ctr = 0, cpart = 0;
 };
 
 Layout make_layout(int64_t M, int64_t K, int64_t N) {
@@ -66,11 +63,6 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
   L.xq = off;     off += align_up(Mp * L.ldk);
   L.xo = off;     off += L.decode ? 0 : align_up(Mp * L.ldk * 2);
   L.wo = off;     off += L.decode ? 0 : align_up(Np * L.ldk * 2);
-  // sized for a 256-CU MI355X; a call on a GPU of another CU count splits
-  // only when that fits (run())
-  L.nsplit = L.decode ? 0 : i8mm::gemm_prefill_nsplit((int)M, (int)N, (int)L.ldk, kLayoutCUs);
-  L.ctr = off;    off += align_up((size_t)L.nsplit * 4);
-  L.cpart = off;  off += (size_t)L.nsplit * 2 * 256 * 256 * 4;
   L.total = off < kAlign ? kAlign : off;
   return L;
 }
@@ -154,19 +146,10 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
   int8_t* xq = out.Xq ? out.Xq : at<int8_t>(ws, L.xq);
   uint16_t* xo = out.X_O ? out.X_O : (L.decode ? nullptr : at<uint16_t>(ws, L.xo));
   uint16_t* wo = out.W_O ? out.W_O : (L.decode ? nullptr : at<uint16_t>(ws, L.wo));
-  // K split in the GEMM (Y output only, within the workspace's capacity):
-  // its counters are zeroed by the row pass of this call
-  int nsplit = 0, nhalf = 0;
-  if (!L.decode && out.C == nullptr && out.Y != nullptr) {
-    const int n_cu = device_cus();
-    if (L.nsplit > 0) {
-      nsplit = i8mm::gemm_prefill_nsplit(m, n, ldk, n_cu);
-      if (nsplit > L.nsplit) nsplit = 0;
-    }
-    // the last round's tiles as halves (needs no workspace)
-    if (nsplit == 0) nhalf = i8mm::gemm_prefill_nhalf(m, n, ldk, n_cu);
-  }
-  int32_t* ctr = nsplit ? at<int32_t>(ws, L.ctr) : nullptr;
+  // prefill GEMM tiles computed as 256x128 halves (Y output only)
+  const int nhalf = !L.decode && out.C == nullptr && out.Y != nullptr
+                        ? i8mm::gemm_prefill_nhalf(m, n, device_cus())
+                        : 0;
 
   if (L.decode && i8mm::activation_small_ok(X, m, k, ldk)) {
     // mask and row codes in one launch; the W_O gather (only when asked
@@ -176,7 +159,7 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
       return hip_fail(e);
     if (wo != nullptr &&
         (e = i8mm::launch_quant_rows(X, 0, k, ldk, bits, nullptr, nullptr, nullptr, nullptr,
-                                     nullptr, Wq, w_scale, n, wo, nullptr, 0, s)) != hipSuccess)
+                                     nullptr, Wq, w_scale, n, wo, s)) != hipSuccess)
       return hip_fail(e);
   } else {
     if (L.decode) {
@@ -192,8 +175,7 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
         return hip_fail(e);
     }
     if ((e = i8mm::launch_quant_rows(X, m, k, ldk, bits, xq, xs, xo, count, out.outlier_idx, Wq,
-                                     w_scale, n, wo, ctr, nsplit,
-                                     s)) != hipSuccess)
+                                     w_scale, n, wo, s)) != hipSuccess)
       return hip_fail(e);
   }
 
@@ -204,9 +186,7 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
                                  ev_start, ev_stop);
   else
     e = i8mm::launch_gemm_prefill(xq, Wq, m, n, k, ldk, xs, w_scale, xo, wo, count, bias, Y,
-                                  out.C, nsplit, nhalf,
-                                  nsplit ? at<int32_t>(ws, L.cpart) : nullptr, ctr, s, ev_start,
-                                  ev_stop);
+                                  out.C, nhalf, s, ev_start, ev_stop);
   if (e != hipSuccess) return hip_fail(e);
   return INT8MM_OK;
 }

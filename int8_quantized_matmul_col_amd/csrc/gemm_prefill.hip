@@ -33,11 +33,10 @@
 // continues the pipeline over the fp16 steps.  |O| is read on the device: no
 // host synchronisation.
 //
-// With few tiles (at most half as many as CUs) each tile is computed by two
-// workgroups that split K and exchange int32 partials.  With a last round of
-// tiles that would fill at most half of the CUs, those tiles are computed as
-// two 256x128 halves each (wave blocks of 128x64), which all run at once in
-// half the time of a whole tile (see k_gemm_prefill).
+// Tiles of a round that would fill at most half of the CUs (a short last
+// round, or all of them when there are few) are computed as two 256x128
+// halves each (wave blocks of 128x64), which all run at once in half the time
+// of a whole tile (see k_gemm_prefill).
 //
 // MFMA operand convention: lane l supplies row (l%32) of its operand and 16
 // bytes of K; both fragments use the same K mapping, so the pairing of K
@@ -438,33 +437,26 @@ __device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restri
 }
 
 // The tile's work after the scales are staged: the int8 pipeline, then the
-// K-split exchange (SPLIT: whole tiles in MODE 0 only), then the C store
-// (MODE 1) or the fused epilogue.  TJ = 4: the whole tile (n0 = its first
-// column); TJ = 2: the half tile h, columns n0 = tile start + 128h on.
-template <int MODE, int TJ, bool SPLIT>
+// C store (MODE 1) or the fused epilogue.  TJ = 4: the whole tile (n0 = its
+// first column); TJ = 2: the half tile h, columns n0 = tile start + 128h on.
+template <int MODE, int TJ>
 __device__ __forceinline__ void tile_work(char* lds, const int8_t* __restrict__ Xq,
                                           const int8_t* __restrict__ Wq, int M, int N, int nk8,
                                           int nk16, const uint16_t* __restrict__ XO,
                                           const uint16_t* __restrict__ WO,
                                           uint16_t* __restrict__ Y, int32_t* __restrict__ C,
-                                          int tm, int tn, int h, int m0, int n0, int su, int half,
-                                          int32_t* __restrict__ cpart, int32_t* __restrict__ ctr) {
-  static_assert(!SPLIT || (MODE == 0 && TJ == 4), "K split: whole tiles, Y output");
-  const bool split = SPLIT;
+                                          int tm, int tn, int h, int m0, int n0) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * (32 * TJ);
   const float* s_x = reinterpret_cast<const float*>(lds + kScaleOff);
   const float* s_w = s_x + BM;
   const float* s_b = s_w + BN;
-  int* s_flag = reinterpret_cast<int*>(lds + kScaleOff + 3 * 1024);
 
-  // this workgroup's int8 steps [k0, k0 + nr); pipeline step s < nr is int8
-  // step k0 + s, then come the outlier steps
-  const int k0 = split && half ? nk8 / 2 : 0;
-  const int nr = split ? (half ? nk8 - nk8 / 2 : nk8 / 2) : nk8;
+  // pipeline step s < nk8 is int8 step s, then come the outlier steps
+  const int nr = nk8;
   Pipe p;
-  make_pipe<TJ>(p, Xq, Wq, XO, WO, tm, tn, h, nk8, k0, nr, nk16, wave, lane);
+  make_pipe<TJ>(p, Xq, Wq, XO, WO, tm, tn, h, nk8, 0, nr, nk16, wave, lane);
 
   v16i acc[TI][TJ];
 #pragma unroll
@@ -474,37 +466,9 @@ __device__ __forceinline__ void tile_work(char* lds, const int8_t* __restrict__ 
 
   Frag<TJ> f0, f1;
   prologue<TJ>(lds, f0, p);
-  // int8 x int8 -> int32 over this workgroup's K steps (outlier columns of
-  // Xq are zero); the loads of the outlier steps ride along
+  // int8 x int8 -> int32 over K (outlier columns of Xq are zero); the loads
+  // of the outlier steps ride along
   run_steps<false, TJ>(lds, acc, f0, f1, p, 0, nr);
-
-  if constexpr (SPLIT) {
-    {
-      // partial of this half, four registers per pass: each lane stores 16
-      // bytes, each wave 1 KiB contiguous
-      constexpr int kQuads = TI * TJ * 4;
-      v4i* mine =
-          reinterpret_cast<v4i*>(cpart) + ((size_t)su * 2 + half) * kQuads * NT + threadIdx.x;
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            mine[((i * TJ + j) * 4 + q) * NT] = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                                    acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-      __builtin_amdgcn_s_waitcnt(0);  // this thread's stores (and every load) have landed
-      __syncthreads();                // ... and every other thread's
-      if (threadIdx.x == 0) {
-        __threadfence();  // the partial is visible device-wide before the count
-        const int first = atomicAdd(&ctr[su], 1) == 0;
-        if (!first) __threadfence();  // and the other half's is seen after it
-        *s_flag = first;
-      }
-      __syncthreads();
-      if (*s_flag) return;  // the other half finishes the tile
-    }
-  }
 
   if constexpr (MODE == 1) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -531,40 +495,8 @@ __device__ __forceinline__ void tile_work(char* lds, const int8_t* __restrict__ 
   __syncthreads();
   const bool vec = (N & 7) == 0;
   char* ys = lds + ((nr + NS - 1) & (NS - 1)) * kStage + wave * 8192;
-  // K split: the other half's int32 partial, added per row group (an exact
-  // integer sum) as it is converted; group i+1's loads are in flight while
-  // group i is finished and stored
-  v4i onext[SPLIT ? TJ : 1][4];
-  const v4i* other = nullptr;
-  if constexpr (SPLIT) {
-    other = reinterpret_cast<const v4i*>(cpart) +
-            ((size_t)su * 2 + (half ^ 1)) * (TI * TJ * 4) * NT + threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) onext[j][q] = other[(j * 4 + q) * NT];
-  }
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
-    if constexpr (SPLIT) {
-      v4i ocur[TJ][4];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ocur[j][q] = onext[j][q];
-      if (i + 1 < TI) {
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) onext[j][q] = other[(((i + 1) * TJ + j) * 4 + q) * NT];
-      }
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += ocur[j][q][e];
-    }
     const float sx = s_x[wm0 + i * 32 + (lane & 31)];
     // the column scales and biases are read again for every row group: held
     // across the groups they would take 32*TJ registers and force spills
@@ -600,54 +532,43 @@ __device__ __forceinline__ void tile_work(char* lds, const int8_t* __restrict__ 
 
 }  // namespace
 
-// SPLIT = false: workgroups 0 .. nwhole-1 compute whole tiles (in workgroup
-// order), then come nhalf half-tile pairs (MODE 0 only): each of the last
-// nhalf tiles is computed as two 256x128 halves by two workgroups 8 apart (so
-// on the same XCD, sharing the A panel in its L2).  Used when the last round
-// of whole tiles would fill at most half of the CUs: its halves then all run
-// at once, in half the time.
-// SPLIT = true (MODE 0): every tile u is computed by two workgroups, u (half
-// 0: int8 steps [0, nk8/2)) and tiles + u (half 1: [nk8/2, nk8)).  Each half
-// stores its int32 partial in cpart; the second to finish (counter ctr[u],
-// zeroed by the activation pass of the same call) adds the other's partial,
-// an exact integer sum, and runs the epilogue.  Used when the tiles would
-// leave most of the GPU idle.  A kernel of its own, so that the registers its
-// exchange needs do not weigh on the whole-tile code.
-template <int MODE, bool SPLIT>  // MODE 0: Y (fused epilogue), 1: int32 C
+// Workgroups 0 .. nwhole-1 compute whole tiles (in workgroup order), then
+// come nhalf half-tile pairs (MODE 0 only): each of the last nhalf tiles is
+// computed as two 256x128 halves by two workgroups 8 apart (so on the same
+// XCD, sharing the A panel in its L2).  Used for a last round of whole tiles
+// that would fill at most half of the CUs (its halves then all run at once,
+// in half the time), and for every tile when there are at most half as many
+// tiles as CUs.  (Halves measured faster there than splitting K between two
+// workgroups that exchange int32 partials: no exchange, and the A panel is
+// read from the L2 twice instead.)
+template <int MODE>  // 0: Y (fused epilogue), 1: int32 C
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
 k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K,
                int ldk, const float* __restrict__ x_scale, const float* __restrict__ w_scale,
                const uint16_t* __restrict__ XO, const uint16_t* __restrict__ WO,
                const int32_t* __restrict__ n_out, const uint16_t* __restrict__ bias,
-               uint16_t* __restrict__ Y, int32_t* __restrict__ C, int nhalf,
-               int32_t* __restrict__ cpart, int32_t* __restrict__ ctr) {
+               uint16_t* __restrict__ Y, int32_t* __restrict__ C, int nhalf) {
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  // su: split unit of this workgroup; ht: a half tile, `half` its column half
-  int tb = (int)blockIdx.x, half = 0, su = -1;
+  // ht: a half tile, `half` its column half
+  int tb = (int)blockIdx.x, half = 0;
   bool ht = false;
-  if constexpr (SPLIT) {
-    su = tb % tiles;
-    half = tb / tiles;
-    tb = su;
-  } else {
-    const int nwhole = tiles - nhalf;
-    if (tb >= nwhole) {
-      // groups of 8 tiles: workgroups bb and bb + 8 of a group of 16 take the
-      // two halves of one tile; the last nhalf % 8 tiles in adjacent pairs
-      const int bb = tb - nwhole;
-      const int g16 = 16 * (nhalf / 8);
-      int t;
-      if (bb < g16) {
-        t = (bb / 16) * 8 + bb % 8;
-        half = (bb / 8) & 1;
-      } else {
-        t = 8 * (nhalf / 8) + (bb - g16) / 2;
-        half = (bb - g16) & 1;
-      }
-      tb = nwhole + t;
-      ht = true;
+  const int nwhole = tiles - nhalf;
+  if (tb >= nwhole) {
+    // groups of 8 tiles: workgroups bb and bb + 8 of a group of 16 take the
+    // two halves of one tile; the last nhalf % 8 tiles in adjacent pairs
+    const int bb = tb - nwhole;
+    const int g16 = 16 * (nhalf / 8);
+    int t;
+    if (bb < g16) {
+      t = (bb / 16) * 8 + bb % 8;
+      half = (bb / 8) & 1;
+    } else {
+      t = 8 * (nhalf / 8) + (bb - g16) / 2;
+      half = (bb - g16) & 1;
     }
+    tb = nwhole + t;
+    ht = true;
   }
   int tm, tn;
   tile_of(tb, M, N, tm, tn);
@@ -668,67 +589,43 @@ k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int
   const int nk8 = ldk / kTileK;
   const int nk16 = MODE == 0 ? (*n_out + 31) / 32 : 0;
   if (MODE == 0 && nk16 > NS - 1) {
-    // whole tile in one workgroup: half 0 of a split unit or of a half-tile
-    // pair (its scales start at the tile's first column) computes it
+    // whole tile in one workgroup: half 0 of a half-tile pair (its scales
+    // start at the tile's first column) computes it
     __syncthreads();  // the tile's scales are in LDS
     if (half == 0) gemm_tile_many(lds, Xq, Wq, M, N, K, ldk, XO, WO, *n_out, Y, tm, tn);
     return;
   }
-  if constexpr (SPLIT) {
-    tile_work<MODE, 4, true>(lds, Xq, Wq, M, N, nk8, nk16, XO, WO, Y, C, tm, tn, 0, m0, n0, su,
-                             half, cpart, ctr);
-  } else {
-    if constexpr (MODE == 0) {
-      if (ht) {
-        tile_work<MODE, 2, false>(lds, Xq, Wq, M, N, nk8, nk16, XO, WO, Y, C, tm, tn, half, m0,
-                                  n0, -1, 0, cpart, ctr);
-        return;
-      }
+  if constexpr (MODE == 0) {
+    if (ht) {
+      tile_work<MODE, 2>(lds, Xq, Wq, M, N, nk8, nk16, XO, WO, Y, C, tm, tn, half, m0, n0);
+      return;
     }
-    tile_work<MODE, 4, false>(lds, Xq, Wq, M, N, nk8, nk16, XO, WO, Y, C, tm, tn, 0, m0, n0, -1,
-                              0, cpart, ctr);
   }
+  tile_work<MODE, 4>(lds, Xq, Wq, M, N, nk8, nk16, XO, WO, Y, C, tm, tn, 0, m0, n0);
 }
 
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, const uint16_t* bias,
-                               uint16_t* Y, int32_t* C, int nsplit, int nhalf, int32_t* cpart,
-                               int32_t* ctr, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                               uint16_t* Y, int32_t* C, int nhalf, hipStream_t s, hipEvent_t e0,
+                               hipEvent_t e1) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  // a K split covers every tile; half tiles, a tail of at most all of them
-  if ((nsplit != 0 && nsplit != tiles) || nhalf < 0 || nhalf > tiles || (nsplit > 0 && nhalf > 0))
-    return hipErrorInvalidValue;
+  if (nhalf < 0 || nhalf > tiles) return hipErrorInvalidValue;
   if (C != nullptr)
-    hipExtLaunchKernelGGL((k_gemm_prefill<1, false>), dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq,
-                          Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, nullptr, Y, C, 0,
-                          nullptr, nullptr);
-  else if (nsplit > 0)
-    hipExtLaunchKernelGGL((k_gemm_prefill<0, true>), dim3(2 * tiles), dim3(NT), 0, s, e0, e1, 0,
-                          Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, bias, Y, C, 0,
-                          cpart, ctr);
+    hipExtLaunchKernelGGL(k_gemm_prefill<1>, dim3(tiles), dim3(NT), 0, s, e0, e1, 0, Xq, Wq, M, N,
+                          K, ldk, x_scale, w_scale, XO, WO, n_out, nullptr, Y, C, 0);
   else
-    hipExtLaunchKernelGGL((k_gemm_prefill<0, false>), dim3(tiles + nhalf), dim3(NT), 0, s, e0, e1,
-                          0, Xq, Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, bias, Y, C,
-                          nhalf, cpart, ctr);
+    hipExtLaunchKernelGGL(k_gemm_prefill<0>, dim3(tiles + nhalf), dim3(NT), 0, s, e0, e1, 0, Xq,
+                          Wq, M, N, K, ldk, x_scale, w_scale, XO, WO, n_out, bias, Y, C, nhalf);
   return hipGetLastError();
 }
 
-int gemm_prefill_nsplit(int M, int N, int ldk, int n_cu) {
+int gemm_prefill_nhalf(int M, int N, int n_cu) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (ldk / kTileK < 32 || n_cu <= 0) return 0;  // short K: the exchange would not pay
-  // Every tile split when the tiles fill at most half of the CUs (one
-  // workgroup per CU).  Splitting only the tiles of a partly filled last
-  // round measured no faster: the exchange of the int32 partials (HBM-bound
-  // when all the split units end together) costs about what it saves.
-  return 2 * tiles <= n_cu ? tiles : 0;
-}
-
-int gemm_prefill_nhalf(int M, int N, int ldk, int n_cu) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (n_cu <= 0 || gemm_prefill_nsplit(M, N, ldk, n_cu) > 0) return 0;
-  // one workgroup per CU: the tiles of a last round that fills at most half
-  // of the CUs run as halves, all at once
+  if (n_cu <= 0) return 0;
+  // one workgroup per CU: every tile when they fill at most half of the CUs,
+  // else the tiles of a last round that fills at most half of them
+  if (2 * tiles <= n_cu) return tiles;
   const int tail = tiles % n_cu;
   return tiles >= n_cu && 2 * tail <= n_cu ? tail : 0;
 }

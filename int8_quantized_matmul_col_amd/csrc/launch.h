@@ -33,28 +33,20 @@ hipError_t launch_colmask(const uint16_t* X, const uint16_t* part, int rc, int M
 hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uint32_t* mask_bits,
                              int8_t* Xq, float* x_scale, uint16_t* XO, int32_t* n_out,
                              int32_t* out_idx, const int8_t* Wq, const float* w_scale, int N,
-                             uint16_t* WO, int32_t* zero_ctr, int n_zero,
-                             hipStream_t s);
+                             uint16_t* WO, hipStream_t s);
 // Prefill tile GEMM: int8 MFMA over K, then fp16 MFMA over the outlier slice,
 // fused dequant epilogue (Y, plus bias[n] when bias != nullptr), or int32
 // accumulators only (C).
-// nsplit (Y only): 0 or the tile count: every tile computed by two
-// workgroups splitting K; int32 partials in cpart (2 * nsplit * 256*256
-// ints), counters ctr (nsplit ints, zero on entry: the row pass of the same
-// call zeroes them).
-// nhalf (Y only, with nsplit == 0): the last nhalf tiles are computed as two
-// 256x128 halves each.
-// hipErrorInvalidValue for any other nsplit / nhalf.
+// nhalf (Y only; 0 .. tile count, else hipErrorInvalidValue): the last nhalf
+// tiles are computed as two 256x128 halves each.
 hipError_t launch_gemm_prefill(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                const float* x_scale, const float* w_scale, const uint16_t* XO,
                                const uint16_t* WO, const int32_t* n_out, const uint16_t* bias,
-                               uint16_t* Y, int32_t* C, int nsplit, int nhalf, int32_t* cpart,
-                               int32_t* ctr, hipStream_t s, hipEvent_t e0 = nullptr,
-                               hipEvent_t e1 = nullptr);
-// How many tiles the GEMM splits for this shape on a GPU of n_cu CUs.
-int gemm_prefill_nsplit(int M, int N, int ldk, int n_cu);
-// How many tiles it computes as halves (0 when it splits).
-int gemm_prefill_nhalf(int M, int N, int ldk, int n_cu);
+                               uint16_t* Y, int32_t* C, int nhalf, hipStream_t s,
+                               hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// How many tiles the GEMM computes as halves for this shape on a GPU of n_cu
+// CUs.
+int gemm_prefill_nhalf(int M, int N, int n_cu);
 // e0/e1 (optional) are stamped by the GEMM dispatch itself: start and end of
 // that kernel, for profiling.
 // Decode (M <= 16): one streaming pass over Wq, outliers handled inline.

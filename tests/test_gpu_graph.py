@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("M,K,N,with_bias", [(300, 1024, 512, False), (300, 1024, 512, True),
-                                             (300, 2112, 520, True),  # split K: counters
+                                             (300, 2112, 520, True),  # every tile as two halves
                                              (8, 2048, 1024, False), (8, 2048, 1024, True)])
 def test_graph_replay_matches_eager(lib, M, K, N, with_bias):
     import torch

@@ -24,9 +24,9 @@ LINEAR_SHAPES = [
     (16, 1024, 1024, 2, 6.0, 0.05),     # decode kernel, one row group per wave
     (5, 3, 7, 1, 0.0, 2.0),             # decode, every column an outlier
     (300, 520, 300, 5, 6.0, 0.5),       # prefill tiles with ragged edges
-    (300, 2112, 520, 7, 6.0, 1.0),      # K split over two workgroups per tile
+    (300, 2112, 520, 7, 6.0, 1.0),      # few tiles: each as two 256x128 halves
     (64, 130, 40, 2, 0.0, 0.5),         # many outlier steps (separate fp16 loop)
-    (260, 2048, 300, 2, 0.0, 30.0),     # split grid + many outlier steps, large bias
+    (260, 2048, 300, 2, 0.0, 30.0),     # half-tile grid + many outlier steps, large bias
     (96, 320, 96, 4, math.inf, 0.5),    # pure int8
 ]
 

@@ -54,8 +54,8 @@ SHAPES = [
     (64, 130, 40, 2, 0.0),         # every non-zero column is an outlier
     (96, 320, 96, 4, math.inf),    # pure int8
     (40, 96, 520, 90, 0.5),        # |O| close to K
-    (300, 2112, 520, 7, 6.0),      # K split over two workgroups per tile, odd step count
-    (260, 2048, 300, 2, 0.0),      # split grid with every column an outlier
+    (300, 2112, 520, 7, 6.0),      # few tiles: each as two 256x128 halves, odd step count
+    (260, 2048, 300, 2, 0.0),      # half-tile grid with every column an outlier
     (300, 9000, 64, 5, 6.0),       # rows too long for one wave: a block per row
     (300, 4700, 64, 5, 6.0),       # row pass held in 10 chunks per lane (4 waves per SIMD)
     (280, 2600, 64, 3, 6.0),       # ... 6 chunks per lane
@@ -194,7 +194,7 @@ def test_output_overflow_gives_inf(lib):
 def test_maximum_k_at_the_int32_bound(lib, M, t):
     # K = the largest accepted: every code is +-127, so |C| reaches
     # 127^2 * K = 2147479576 (just below 2^31) with no outlier column, on
-    # both kernels (decode M <= 16, prefill with its K split); with t = 6
+    # both kernels (decode M <= 16, prefill in 256x128 half tiles); with t = 6
     # three planted columns leave the int8 part
     K, N = 133144, 64
     print(f"case max K M={M} K={K} N={N} t={t}", flush=True)

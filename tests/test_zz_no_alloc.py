@@ -48,7 +48,7 @@ def _pair(mm, M, K, N, n_out, t, seed):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("first,second", [
-    # tile GEMM (with the K split at 2112 columns), then a smaller prefill call
+    # tile GEMM (few tiles, each as two halves), then a smaller prefill call
     ((300, 2112, 520, 7, 6.0), (33, 64, 40, 2, 6.0)),
     # many outlier columns (t = 0: every column fp16), then few
     ((96, 320, 96, 4, 0.0), (40, 96, 72, 3, 6.0)),

@@ -28,6 +28,13 @@ constexpr int kSlots = 8;  // outlier K steps parked in LDS (more: static schedu
 constexpr int kMaxWords = (133144 + 63) / 64 * 2;  // mask words for the largest K
 }  // namespace
 
+// A 16-byte Wq fragment.  The weight is read once per call and never again
+// in it: nontemporal loads (measured 4.95 -> 5.55 TB/s over the
+// 8192 x 28672 weight) keep it from displacing what the caches do reuse.
+__device__ __forceinline__ v4i wload(const int8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
+
 template <int G, int MODE>  // MODE 0: Y, 1: int32 C
 __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K, int ldk,
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
         const int sl = min(base + u, nsteps - 1);  // a short last chunk re-reads, not counted
         const size_t off = (size_t)sl * kTileBytes;
 #pragma unroll
-        for (int g = 0; g < G; ++g) b[u][g] = *reinterpret_cast<const v4i*>(wrow[g] + off);
+        for (int g = 0; g < G; ++g) b[u][g] = wload(wrow[g] + off);
         a[u] = (xvalid && base + u < nsteps) ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
       }
 #pragma unroll
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
       for (int u = 0; u < kU; ++u) {
         const size_t off = (size_t)(s + u) * kTileBytes;
 #pragma unroll
-        for (int g = 0; g < G; ++g) b[u][g] = *reinterpret_cast<const v4i*>(wrow[g] + off);
+        for (int g = 0; g < G; ++g) b[u][g] = wload(wrow[g] + off);
         a[u] = xvalid ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
       }
 #pragma unroll
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
       const size_t off = (size_t)s * kTileBytes;
       v4i b[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) b[g] = *reinterpret_cast<const v4i*>(wrow[g] + off);
+      for (int g = 0; g < G; ++g) b[g] = wload(wrow[g] + off);
       const v4i a = xvalid ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
 #pragma unroll
       for (int g = 0; g < G; ++g) acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[g], acc[g], 0, 0, 0);

@@ -26,6 +26,14 @@ __device__ __forceinline__ uint16_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// Two floats -> two binary16 (round to nearest even), packed low | high<<16:
+// one v_cvt_pk_f16_f32 on gfx950.
+__device__ __forceinline__ uint32_t f2h2(float lo, float hi) {
+  typedef float v2f_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_t{lo, hi}), v2h_t));
+}
+
 // |x| of a finite binary16 value, as its bit pattern: for non-negative
 // finite values the bit patterns order like the values.
 __device__ __forceinline__ uint32_t habs_bits(uint32_t bits) { return bits & 0x7fffu; }

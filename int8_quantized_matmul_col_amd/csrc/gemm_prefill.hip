@@ -322,8 +322,10 @@ __device__ __forceinline__ void tile_of(int b, int M, int N, int& tm, int& tn) {
 // rows): each lane writes its 4-column runs as 8-byte pieces (piece e of row
 // r at position e ^ 2*((r/2)%16), which spreads the rows of a write over the
 // banks), then reads back whole 16-byte pieces for row-segment stores of
-// 64*TJ bytes.
-template <int TJ>
+// 64*TJ bytes.  INTERIOR: the whole block lies inside Y and N % 8 == 0, so the
+// stores need no checks (branches around every store measured a large part
+// of the epilogue).
+template <int TJ, bool INTERIOR>
 __device__ __forceinline__ void store_rows(const v16f (&y)[TJ], char* ys, uint16_t* __restrict__ Y,
                                            int M, int N, int m_base, int n_base, bool vec,
                                            int lane) {
@@ -335,8 +337,8 @@ __device__ __forceinline__ void store_rows(const v16f (&y)[TJ], char* ys, uint16
     for (int q = 0; q < 4; ++q) {
       const int e = j * 8 + q * 2 + (lane >> 5);
       uint2 v;
-      v.x = (uint32_t)f2h(y[j][4 * q]) | ((uint32_t)f2h(y[j][4 * q + 1]) << 16);
-      v.y = (uint32_t)f2h(y[j][4 * q + 2]) | ((uint32_t)f2h(y[j][4 * q + 3]) << 16);
+      v.x = f2h2(y[j][4 * q], y[j][4 * q + 1]);
+      v.y = f2h2(y[j][4 * q + 2], y[j][4 * q + 3]);
       *reinterpret_cast<uint2*>(ys + row * 256 + (e ^ sw) * 8) = v;
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -345,22 +347,36 @@ __device__ __forceinline__ void store_rows(const v16f (&y)[TJ], char* ys, uint16
   constexpr int PR = 4 * TJ;   // 16-byte pieces of a row segment
   constexpr int RPP = 64 / PR;  // rows per pass
   const int c = lane % PR;
-  const int n_col = n_base + c * 8;
+  if constexpr (INTERIOR) {
+    // a uniform block base and one per-lane element offset for every pass
+    uint16_t* yb = Y + (size_t)m_base * N + n_base;
+    const uint32_t loff = (uint32_t)((lane / PR) * N + c * 8);
 #pragma unroll
-  for (int pp = 0; pp < 32 / RPP; ++pp) {
-    const int rl = pp * RPP + lane / PR;
-    const int m = m_base + rl;
-    const int pos = (2 * c) ^ (2 * ((rl >> 1) & 15));  // even: the pair stays in order
-    const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 256 + pos * 8);
-    if (m < M) {
-      if (vec && n_col + 8 <= N) {
-        // Y is written once and not read again here: stream it past the caches
-        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col));
-      } else {
-        const uint16_t* hh = reinterpret_cast<const uint16_t*>(&v);
+    for (int pp = 0; pp < 32 / RPP; ++pp) {
+      const int rl = pp * RPP + lane / PR;
+      const int pos = (2 * c) ^ (2 * ((rl >> 1) & 15));  // even: the pair stays in order
+      const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 256 + pos * 8);
+      // Y is written once and not read again here: stream it past the caches
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<v4i*>(yb + (size_t)(pp * RPP) * N + loff));
+    }
+  } else {
+    const int n_col = n_base + c * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (n_col + e < N) Y[(size_t)m * N + n_col + e] = hh[e];
+    for (int pp = 0; pp < 32 / RPP; ++pp) {
+      const int rl = pp * RPP + lane / PR;
+      const int m = m_base + rl;
+      const int pos = (2 * c) ^ (2 * ((rl >> 1) & 15));
+      const v4i v = *reinterpret_cast<const v4i*>(ys + rl * 256 + pos * 8);
+      if (m < M) {
+        if (vec && n_col + 8 <= N) {
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(Y + (size_t)m * N + n_col));
+        } else {
+          const uint16_t* hh = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n_col + e < N) Y[(size_t)m * N + n_col + e] = hh[e];
+        }
       }
     }
   }
@@ -427,12 +443,83 @@ __device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restri
   __syncthreads();
   const bool vec = (N & 7) == 0;
   char* ys = lds + wave * 8192;
+  const bool interior = vec && m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
     v16f y[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) y[j] = __builtin_bit_cast(v16f, acc[i][j]);
-    store_rows<TJ>(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
+    if (interior)
+      store_rows<TJ, true>(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
+    else
+      store_rows<TJ, false>(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
+  }
+}
+
+// Few outlier steps (at most NS-1): pipeline steps nr .. nr+nk16-1 sit in
+// LDS stages (nr+st)%NS, loaded by the int8 loop; stage (nr-1)%NS, the last
+// int8 step's, is free once every load has landed (the loads past the last
+// step that targeted it fetched nothing) and stages Y (8 KiB per wave).  Per
+// 32-row group i: Y = fp32(C)*s + b straight from the int32 accumulators,
+// the outlier products accumulated on top, fp16 rows stored.
+template <int TJ, bool INTERIOR>
+__device__ __forceinline__ void epilogue_few(char* lds, v16i (&acc)[TI][TJ], const Pipe& p, int nr,
+                                             int nk16, char* ys, uint16_t* __restrict__ Y, int M,
+                                             int N, int m0, int n0, bool vec) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * (32 * TJ);
+  const float* s_x = reinterpret_cast<const float*>(lds + kScaleOff);
+  const float* s_w = s_x + BM;
+  const float* s_b = s_w + BN;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const float sx = s_x[wm0 + i * 32 + (lane & 31)];
+    // the column scales and biases are read again for every row group: held
+    // across the groups they would take 32*TJ registers and force spills
+    int cb = wn0 + (lane >> 5) * 4;
+    asm volatile("" : "+v"(cb));
+    // fp32(C)*s + b written back into the group's own accumulator registers
+    // (as fp32 bit patterns): the outlier MFMAs then accumulate where the
+    // values already are (a separate fp32 copy measured ~4x slower, the
+    // compiler moving it between register files around every MFMA)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = cb + j * 32 + q * 8;
+        const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[c]);
+        const v4f b4 = *reinterpret_cast<const v4f*>(&s_b[c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[i][j][4 * q + e] =
+              __float_as_int((float)acc[i][j][4 * q + e] * (sx * w4[e]) + b4[e]);
+      }
+    for (int st = 0; st < nk16; ++st) {
+      const uint32_t sb = (uint32_t)((nr + st) & (NS - 1)) * kStage;
+      // all of the step's fragments first, so the reads overlap instead of
+      // each MFMA waiting on the one read before it
+      v4i a[2], bb[2][TJ];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        a[kk] = lread(lds, sb + p.ra[kk] + i * 2048);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) bb[kk][j] = lread(lds, sb + p.rb[kk] + j * 2048);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_bit_cast(
+              v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(v8h, bb[kk][j]), __builtin_bit_cast(v8h, a[kk]),
+                        __builtin_bit_cast(v16f, acc[i][j]), 0, 0, 0));
+    }
+    v16f y[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) y[j] = __builtin_bit_cast(v16f, acc[i][j]);
+    store_rows<TJ, INTERIOR>(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
   }
 }
 
@@ -449,9 +536,6 @@ __device__ __forceinline__ void tile_work(char* lds, const int8_t* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * (32 * TJ);
-  const float* s_x = reinterpret_cast<const float*>(lds + kScaleOff);
-  const float* s_w = s_x + BM;
-  const float* s_b = s_w + BN;
 
   // pipeline step s < nk8 is int8 step s, then come the outlier steps
   const int nr = nk8;
@@ -485,49 +569,17 @@ __device__ __forceinline__ void tile_work(char* lds, const int8_t* __restrict__ 
     return;
   }
 
-  // Few outlier steps (at most NS-1): pipeline steps nr .. nr+nk16-1 sit in
-  // LDS stages (nr+st)%NS, loaded by the int8 loop; stage (nr-1)%NS, the last
-  // int8 step's, is free once every load has landed (the loads past the last
-  // step that targeted it fetched nothing) and stages Y (8 KiB per wave).  Per
-  // 32-row group i: Y = fp32(C)*s + b straight from the int32 accumulators,
-  // the outlier products accumulated on top, fp16 rows stored.
+  // few outlier steps: the epilogue (see epilogue_few)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const bool vec = (N & 7) == 0;
   char* ys = lds + ((nr + NS - 1) & (NS - 1)) * kStage + wave * 8192;
-#pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const float sx = s_x[wm0 + i * 32 + (lane & 31)];
-    // the column scales and biases are read again for every row group: held
-    // across the groups they would take 32*TJ registers and force spills
-    int cb = wn0 + (lane >> 5) * 4;
-    asm volatile("" : "+v"(cb));
-    v16f y[TJ];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = cb + j * 32 + q * 8;
-        const v4f w4 = *reinterpret_cast<const v4f*>(&s_w[c]);
-        const v4f b4 = *reinterpret_cast<const v4f*>(&s_b[c]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          y[j][4 * q + e] = (float)acc[i][j][4 * q + e] * (sx * w4[e]) + b4[e];
-      }
-    for (int st = 0; st < nk16; ++st) {
-      const uint32_t sb = (uint32_t)((nr + st) & (NS - 1)) * kStage;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const v8h a = __builtin_bit_cast(v8h, lread(lds, sb + p.ra[kk] + i * 2048));
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const v8h bb = __builtin_bit_cast(v8h, lread(lds, sb + p.rb[kk] + j * 2048));
-          y[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bb, a, y[j], 0, 0, 0);
-        }
-      }
-    }
-    store_rows<TJ>(y, ys, Y, M, N, m0 + wm0 + i * 32, n0 + wn0, vec, lane);
-  }
+  // a uniform branch: tiles wholly inside Y (all but the ragged edge) store
+  // without checks
+  if (vec && m0 + BM <= M && n0 + 64 * TJ <= N)
+    epilogue_few<TJ, true>(lds, acc, p, nr, nk16, ys, Y, M, N, m0, n0, vec);
+  else
+    epilogue_few<TJ, false>(lds, acc, p, nr, nk16, ys, Y, M, N, m0, n0, vec);
 }
 
 }  // namespace

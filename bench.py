@@ -35,6 +35,11 @@ of 10 more calls against HBM bandwidth).  Prints one JSON line.
 * per_call   -- median and minimum of per-call times (HIP events around each
                whole call, and the kernel's own stamps), from passes after
                the timed region.
+* ceilings   -- after the timed regions, the practical ceilings of this GPU
+               from the probe library (libint8mm_ceilings.so): the int8 MFMA
+               issue rate on random and on zero operands, and the read rate of
+               a 2 GiB contiguous-chunk stream; roofline.frac_of_measured_ceiling
+               sets each matmul kernel against the matching one.
 * cpu_baseline -- the CPU oracle (oracle/, unchanged) timed on this host: on a
                row sample of the headline workload with all BLAS threads, and
                single-threaded on the tiny and the M = 16 decode workloads; the
@@ -501,6 +506,60 @@ def measure(mm, lib, ev, dev, case, t, steps, warmup, rotate=None, others=False,
     return res
 
 
+PROBE_LIB = os.path.join(ROOT, "int8_quantized_matmul_col_amd", "libint8mm_ceilings.so")
+
+
+def measure_ceilings(torch, dev) -> dict:
+    """The practical ceilings on this GPU (after the timed regions): the int8
+    MFMA issue rate on random and on zero operands, and the HBM read rate of a
+    contiguous-chunk stream over 2 GiB (beyond the 256 MB MALL)."""
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} missing: run __graft_entry__.build()")
+    pl = ctypes.CDLL(PROBE_LIB)
+    pl.int8mm_probe_mfma_i8.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    pl.int8mm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    g = torch.Generator().manual_seed(7)
+    rnd = torch.randint(-128, 128, (65536,), dtype=torch.int8, generator=g).to(dev)
+    zero = torch.zeros(65536, dtype=torch.int8, device=dev)
+    blocks = 256 * 4  # four workgroups of 4 waves per CU: 4 waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    res = {}
+    for name, src in (("random", rnd), ("zero", zero)):
+        v = ctypes.c_double()
+        st = pl.int8mm_probe_mfma_i8(ctypes.c_void_p(src.data_ptr()), blocks, 2000,
+                                     ctypes.c_void_p(out.data_ptr()), ctypes.byref(v))
+        if st != 0:
+            raise SystemExit(f"MFMA probe failed: HIP error {st}")
+        res[f"mfma_i8_{name}_operands_TOPS"] = round(v.value / 1e12, 1)
+    rb = 2 << 30
+    buf = torch.ones(rb // 4, dtype=torch.int32, device=dev)
+    rblocks = 2048
+    rout = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
+    v = ctypes.c_double()
+    st = pl.int8mm_probe_read(ctypes.c_void_p(buf.data_ptr()), rb, rblocks,
+                              ctypes.c_void_p(rout.data_ptr()), ctypes.byref(v))
+    if st != 0:
+        raise SystemExit(f"read probe failed: HIP error {st}")
+    res["hbm_read_GB/s"] = round(v.value / 1e9, 1)
+    res["method"] = ("int8mm_probe_mfma_i8: 4 waves per SIMD, 16 independent "
+                     "v_mfma_i32_32x32x32_i8 accumulators each, 2000 iterations; "
+                     "int8mm_probe_read: 2048 workgroups, each a contiguous chunk of 2 GiB, "
+                     "8 x 16-byte loads per lane in flight (libint8mm_ceilings.so)")
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
+def frac_of_ceiling(roof: dict, ceil: dict):
+    if roof["unit"] == "GB/s":
+        return round(roof["achieved"] / ceil["hbm_read_GB/s"], 4)
+    if roof["peak"] >= 4999.0:  # int8 MFMA peak: against the random-operand rate
+        return round(roof["achieved"] / ceil["mfma_i8_random_operands_TOPS"], 4)
+    return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -515,6 +574,8 @@ def main() -> int:
                     help="weight copies cycled through (default: at least 768 MiB of weights, "
                          "so that every call reads its weight from HBM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the MFMA / HBM ceiling probes run after the timed regions")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a copy-like elementwise kernel (torch.neg) over "
                          f"{COPY_CAL_BYTES >> 20} MiB so HBM counters can be scaled to known bytes")
@@ -566,6 +627,14 @@ def main() -> int:
         log(f"[bench] {name}: {r['ms_per_step']} ms per call, kernel {r['roofline']['kernel_ms']} ms, "
             f"frac {r['roofline']['frac']}")
 
+    ceilings = None
+    if not args.no_ceilings:
+        log("[bench] measuring the MFMA and HBM ceilings ...")
+        ceilings = measure_ceilings(torch, dev)
+        head["roofline"]["frac_of_measured_ceiling"] = frac_of_ceiling(head["roofline"], ceilings)
+        for r in extra.values():
+            r["roofline"]["frac_of_measured_ceiling"] = frac_of_ceiling(r["roofline"], ceilings)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
@@ -596,6 +665,7 @@ def main() -> int:
         "prepare_weight": head["prepare_weight"],
         "other_entry_points": head.get("other_entry_points"),
         "extra": extra,
+        "ceilings": ceilings,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out), flush=True)

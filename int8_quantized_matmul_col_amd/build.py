@@ -3,7 +3,9 @@
     python -m int8_quantized_matmul_col_amd.build
 
 Each source is compiled to an object under ``_build/`` (in parallel), then
-linked into ``int8_quantized_matmul_col_amd/libint8mm.so``.  Flags:
+linked into ``int8_quantized_matmul_col_amd/libint8mm.so``.  The measurement
+probes (``csrc/ceilings.hip``) become a library of their own,
+``libint8mm_ceilings.so``, which only the benchmark loads.  Flags:
 
 * ``--offload-arch=gfx950`` only (MI355X).
 * No fast-math: the quantizer relies on IEEE-correctly-rounded fp32 division.
@@ -25,6 +27,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libint8mm.so")
+PROBE_LIB_PATH = os.path.join(HERE, "libint8mm_ceilings.so")
+PROBE_SOURCES = ["ceilings.hip"]
 
 SOURCES = ["api.hip", "prepare.hip", "activation.hip", "gemm_prefill.hip", "gemm_decode.hip"]
 HEADERS = ["device_common.h", "launch.h"]
@@ -65,19 +69,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every source and links libint8mm.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source, links libint8mm.so and the probe library;
+    returns the path of libint8mm.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

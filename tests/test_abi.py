@@ -52,6 +52,17 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_probe_library_loads_and_exports_the_probes(lib):
+    """The measurement probes the benchmark loads live in a library of their
+    own, outside the matmul ABI."""
+    from int8_quantized_matmul_col_amd import build
+    assert os.path.exists(build.PROBE_LIB_PATH)
+    probes = ctypes.CDLL(build.PROBE_LIB_PATH)
+    for name in ("int8mm_probe_mfma_i8", "int8mm_probe_read"):
+        assert hasattr(probes, name), name
+    assert not hasattr(lib, "int8mm_probe_read")
+
+
 def test_header_constants_match_binding():
     src = open(HEADER).read()
     consts = dict(re.findall(r"#define (INT8MM_\w+) \(?(-?\d+)\)?", src))

@@ -207,25 +207,42 @@ namespace {
 // mask bits ob (bit i = column i is an outlier) expanded to keep-masks.
 __device__ __forceinline__ uint32_t keep_bytes(uint32_t ob4) {
   // bit i of ob4 (< 16) moved to bit 8i (the shifted copies do not overlap),
-  // then widened to the whole byte
+  // then a byte permute turns each byte into 0x00 (bit set: selector 12) or
+  // 0xff (bit clear: selector 13); no full-width multiply
   const uint32_t lsb = (ob4 * 0x00204081u) & 0x01010101u;
-  return ~(lsb * 0xffu);
+  return __builtin_amdgcn_perm(0u, 0u, 0x0d0d0d0du - lsb);
 }
-__device__ __forceinline__ uint32_t keep_halves(uint32_t ob2) {
-  return ((ob2 & 1u) ? 0u : 0xffffu) | ((ob2 & 2u) ? 0u : 0xffff0000u);
+// Clear-masks of the outlier columns of one 8-column chunk (mask bits ob,
+// bit i = column i), branch-free: v_perm's selectors 8 and 9 fill a byte
+// with bit 15 or bit 31 of its second source (10 and 11: of its first), so
+// with mask bits moved to bits 15 and 31 of shifted copies of ob, one permute
+// makes one mask word.  s3 holds bits 6 and 7 there, s2 bits 4 and 5, s1
+// bits 2 and 3, s0 bits 0 and 1 (no other bit of ob reaches 15 or 31).
+struct ChunkMasks {
+  uint32_t h[4];  // binary16 pair p: 0xffff over column 2p and/or 2p+1 if outliers
+  uint32_t b[2];  // code bytes 0-3 and 4-7: 0xff over each outlier column
+};
+__device__ __forceinline__ ChunkMasks chunk_masks(uint32_t ob) {
+  const uint32_t s3 = (ob << 9) | (ob << 24);
+  const uint32_t s2 = s3 << 2, s1 = s3 << 4, s0 = s3 << 6;
+  ChunkMasks m;
+  m.h[0] = __builtin_amdgcn_perm(0u, s0, 0x09090808u);
+  m.h[1] = __builtin_amdgcn_perm(0u, s1, 0x09090808u);
+  m.h[2] = __builtin_amdgcn_perm(0u, s2, 0x09090808u);
+  m.h[3] = __builtin_amdgcn_perm(0u, s3, 0x09090808u);
+  m.b[0] = __builtin_amdgcn_perm(s1, s0, 0x0b0a0908u);
+  m.b[1] = __builtin_amdgcn_perm(s3, s2, 0x0b0a0908u);
+  return m;
 }
 
 // Packed |x| maxima (two 16-bit lanes) of the regular columns of a chunk.
-__device__ __forceinline__ uint32_t chunk_absmax2(const uint4& w, uint32_t ob) {
-  uint32_t d0 = w.x & 0x7fff7fffu, d1 = w.y & 0x7fff7fffu;
-  uint32_t d2 = w.z & 0x7fff7fffu, d3 = w.w & 0x7fff7fffu;
-  if (ob) {
-    d0 &= keep_halves(ob & 3u);
-    d1 &= keep_halves((ob >> 2) & 3u);
-    d2 &= keep_halves((ob >> 4) & 3u);
-    d3 &= keep_halves((ob >> 6) & 3u);
-  }
+__device__ __forceinline__ uint32_t chunk_absmax2(const uint4& w, const ChunkMasks& m) {
+  const uint32_t d0 = w.x & ~m.h[0] & 0x7fff7fffu, d1 = w.y & ~m.h[1] & 0x7fff7fffu;
+  const uint32_t d2 = w.z & ~m.h[2] & 0x7fff7fffu, d3 = w.w & ~m.h[3] & 0x7fff7fffu;
   return pk_max_u16(pk_max_u16(d0, d1), pk_max_u16(d2, d3));
+}
+__device__ __forceinline__ uint32_t chunk_absmax2(const uint4& w, uint32_t ob) {
+  return chunk_absmax2(w, chunk_masks(ob));
 }
 
 // Outlier columns of one chunk of row m (mask bits ob = (word >> sh) & 0xff,
@@ -267,21 +284,23 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 
 // Chunks rl, rl + LPR, ... of one row into registers, zeros from chunk nck
 // = K/8 on; the row is 16-byte aligned and K % 8 == 0 (the register-resident
-// form is used only then).
-template <int CPL, int LPR>
+// form is used only then).  FULL: the row is exactly CPL*LPR chunks (K = ldk
+// = 8*CPL*LPR), so every lane loads, quantizes and stores all CPL of its
+// chunks with no per-chunk test.
+template <int CPL, int LPR, bool FULL>
 __device__ __forceinline__ void load_row(uint4 (&h)[CPL > 0 ? CPL : 1], const uint16_t* row, int rl,
                                          int nck) {
 #pragma unroll
   for (int u = 0; u < CPL; ++u) {
     const int c = rl + u * LPR;
-    h[u] = c < nck ? reinterpret_cast<const uint4*>(row)[c] : uint4{0u, 0u, 0u, 0u};
+    h[u] = FULL || c < nck ? reinterpret_cast<const uint4*>(row)[c] : uint4{0u, 0u, 0u, 0u};
   }
 }
 
 // Mask bytes of the chunks of lane rl (byte u of obs[u / 4] = mask bits of
 // chunk rl + u*LPR): the same for every row, so they are gathered once per
 // block.
-template <int CPL, int LPR>
+template <int CPL, int LPR, bool FULL>
 __device__ __forceinline__ void chunk_mask_bytes(uint32_t (&obs)[(CPL + 3) / 4 > 0 ? (CPL + 3) / 4 : 1],
                                                  const uint32_t* s_bits, int rl, int nch) {
 #pragma unroll
@@ -289,7 +308,7 @@ __device__ __forceinline__ void chunk_mask_bytes(uint32_t (&obs)[(CPL + 3) / 4 >
 #pragma unroll
   for (int u = 0; u < CPL; ++u) {
     const int c = rl + u * LPR;
-    const uint32_t ob = c < nch ? (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u;
+    const uint32_t ob = FULL || c < nch ? (s_bits[c >> 2] >> ((c & 3) * 8)) & 0xffu : 0u;
     obs[u >> 2] |= ob << ((u & 3) * 8);
   }
 }
@@ -304,7 +323,7 @@ struct OutlierRow {
 // One row m (< M) held in registers (CPL > 0): absmax of |x| over the
 // regular columns, codes (zero on the outlier columns), stores.  With
 // WPR == 4 the block's four waves share the row (block barriers inside).
-template <int WPR, int CPL>
+template <int WPR, int CPL, bool FULL>
 __device__ __forceinline__ void quant_row_regs(uint4 (&h)[CPL > 0 ? CPL : 1],
                                                const uint32_t (&obs)[(CPL + 3) / 4 > 0 ? (CPL + 3) / 4 : 1],
                                                const uint16_t* __restrict__ X, int m, int K,
@@ -359,18 +378,28 @@ __device__ __forceinline__ void quant_row_regs(uint4 (&h)[CPL > 0 ? CPL : 1],
   // codes chunk by chunk, each stored at once: the fast quotient, the exact
   // one for a chunk with a value near a half-integer, outlier columns zeroed.
   // Chunk c = rl + u*LPR starts at byte 8c of the row: LPR*8/64 column
-  // blocks (of kTileBytes each) after chunk rl.
-  int8_t* xq_lane = Xq + tiled_offset(m, (size_t)rl * 8, ldk);
-  constexpr size_t kStep = (size_t)LPR * 8 / kTileK * kTileBytes;
+  // blocks (of kTileBytes each) after chunk rl.  The stores address the
+  // row's 256-row panel (a base the whole wave shares: m is the same in every
+  // lane) plus one 32-bit lane offset, kept in a register (left visible, the
+  // compiler recomputes the 64-bit tiled offset for every chunk).
+  const int mu = __builtin_amdgcn_readfirstlane(m);
+  int8_t* xq_panel = Xq + (size_t)(mu >> 8) * kPanelRows * (size_t)ldk;
+  uint32_t xoff = (uint32_t)(tiled_offset(mu & 255, (size_t)rl * 8, ldk));
+  asm volatile("" : "+v"(xoff));
+  constexpr uint32_t kStep = (uint32_t)(LPR * 8 / kTileK * kTileBytes);
 #pragma unroll
   for (int u = 0; u < CPL; ++u) {
     float dev;
     uint2 q = quant8_fast(h[u], r, &dev);
     if (dev > kTieGuard) q = quant8_exact(h[u], a);
-    const uint32_t ob = (ob_row[u >> 2] >> ((u & 3) * 8)) & 0xffu;
-    q.x &= keep_bytes(ob & 0xfu);
-    q.y &= keep_bytes(ob >> 4);
-    if (rl + u * LPR < nch) *reinterpret_cast<uint2*>(xq_lane + u * kStep) = q;
+    // the masks again (a few permutes), not held from the absmax pass
+    uint32_t obq = (ob_row[u >> 2] >> ((u & 3) * 8)) & 0xffu;
+    asm volatile("" : "+v"(obq));
+    const ChunkMasks cm = chunk_masks(obq);
+    q.x &= ~cm.b[0];
+    q.y &= ~cm.b[1];
+    if (FULL || rl + u * LPR < nch)
+      *reinterpret_cast<uint2*>(xq_panel + (xoff + (uint32_t)u * kStep)) = q;
   }
   if (XO != nullptr) {
     if (xo_one_pass) {
@@ -476,7 +505,7 @@ __device__ __forceinline__ int row_group_of(int rb, int n_row_blocks) {
 constexpr int kWoRows = 16;
 constexpr int kRowBlocks = 2048;  // row blocks of the one-wave-per-row form
 
-template <int WPR, int CPL>
+template <int WPR, int CPL, bool FULL>
 __device__ __forceinline__ void quant_rows_body(
     const uint16_t* __restrict__ X, int M, int K, int ldk, int vec, int n_wo_blocks,
     const uint32_t* __restrict__ mask_bits, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
@@ -502,7 +531,7 @@ __device__ __forceinline__ void quant_rows_body(
   // memory latencies overlap
   uint4 ha[CPL > 0 ? CPL : 1];
   const int nck = K >> 3;  // whole 8-column chunks of a row (K % 8 == 0 when CPL > 0)
-  if (CPL > 0 && rb >= 0 && m < M) load_row<CPL, LPR>(ha, X + (size_t)m * K, rl, nck);
+  if (CPL > 0 && rb >= 0 && m < M) load_row<CPL, LPR, FULL>(ha, X + (size_t)m * K, rl, nck);
   const int total = load_mask_prefix(mask_bits, nw, s_bits, s_pre);
   const int opad = (total + 63) & ~63;
   // the O list in LDS when it fits (W_O gather, X_O slice)
@@ -574,10 +603,10 @@ __device__ __forceinline__ void quant_rows_body(
   // ---- rows m, m + mstride, ... (one pass for M <= 4 * kRowBlocks)
   if (CPL > 0) {
     uint32_t obs[(CPL + 3) / 4 > 0 ? (CPL + 3) / 4 : 1];
-    chunk_mask_bytes<CPL, LPR>(obs, s_bits, rl, nch);
+    chunk_mask_bytes<CPL, LPR, FULL>(obs, s_bits, rl, nch);
     for (bool first = true; m < M; m += mstride, first = false) {
-      if (!first) load_row<CPL, LPR>(ha, X + (size_t)m * K, rl, nck);
-      quant_row_regs<WPR, CPL>(ha, obs, X, m, K, ldk, rl, nch, total, opad, s_bits, s_pre,
+      if (!first) load_row<CPL, LPR, FULL>(ha, X + (size_t)m * K, rl, nck);
+      quant_row_regs<WPR, CPL, FULL>(ha, obs, X, m, K, ldk, rl, nch, total, opad, s_bits, s_pre,
                                s_olist, olist_in_lds, nw, s_red, Xq, x_scale, XO);
     }
   } else {
@@ -593,17 +622,17 @@ __device__ __forceinline__ void quant_rows_body(
       float *__restrict__ x_scale, uint16_t *__restrict__ XO, int32_t *__restrict__ n_out,     \
       int32_t *__restrict__ out_idx, const int8_t *__restrict__ Wq,                             \
       const float *__restrict__ w_scale, int N, uint16_t *__restrict__ WO
-template <int WPR, int CPL>
+template <int WPR, int CPL, bool FULL>
 __global__ __launch_bounds__(256) void k_quant_rows(I8MM_QUANT_ROWS_ARGS) {
-  quant_rows_body<WPR, CPL>(X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out,
+  quant_rows_body<WPR, CPL, FULL>(X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out,
                             out_idx, Wq, w_scale, N, WO);
 }
 // The same held to 128 registers (4 waves per SIMD: a wave per row for 16
 // rows per CU at once)
-template <int WPR, int CPL>
+template <int WPR, int CPL, bool FULL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_quant_rows4(
     I8MM_QUANT_ROWS_ARGS) {
-  quant_rows_body<WPR, CPL>(X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out,
+  quant_rows_body<WPR, CPL, FULL>(X, M, K, ldk, vec, n_wo_blocks, mask_bits, Xq, x_scale, XO, n_out,
                             out_idx, Wq, w_scale, N, WO);
 }
 #undef I8MM_QUANT_ROWS_ARGS
@@ -752,17 +781,33 @@ hipError_t launch_colmask(const uint16_t* X, const uint16_t* part, int rc, int M
   return hipGetLastError();
 }
 
+template <int WPR, int CPL, bool FULL>
+static void launch_qr1(dim3 grid, size_t lds, hipStream_t s, const uint16_t* X, int M, int K,
+                       int ldk, int vec, int nwb, const uint32_t* mb, int8_t* Xq, float* xs,
+                       uint16_t* XO, int32_t* n_out, int32_t* out_idx, const int8_t* Wq,
+                       const float* ws, int N, uint16_t* WO) {
+  if constexpr (WPR == 1 && CPL == 10)
+    hipLaunchKernelGGL((k_quant_rows4<WPR, CPL, FULL>), grid, dim3(256), lds, s, X, M, K, ldk,
+                       vec, nwb, mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO);
+  else
+    hipLaunchKernelGGL((k_quant_rows<WPR, CPL, FULL>), grid, dim3(256), lds, s, X, M, K, ldk,
+                       vec, nwb, mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO);
+}
+// FULL when the row is exactly the form's CPL*64*WPR chunks (K = ldk)
 template <int WPR, int CPL>
 static void launch_qr(dim3 grid, size_t lds, hipStream_t s, const uint16_t* X, int M, int K,
                       int ldk, int vec, int nwb, const uint32_t* mb, int8_t* Xq, float* xs,
                       uint16_t* XO, int32_t* n_out, int32_t* out_idx, const int8_t* Wq,
                       const float* ws, int N, uint16_t* WO) {
-  if (WPR == 1 && CPL == 10)
-    hipLaunchKernelGGL((k_quant_rows4<WPR, CPL>), grid, dim3(256), lds, s, X, M, K, ldk, vec, nwb,
-                       mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO);
-  else
-    hipLaunchKernelGGL((k_quant_rows<WPR, CPL>), grid, dim3(256), lds, s, X, M, K, ldk, vec, nwb,
-                       mb, Xq, xs, XO, n_out, out_idx, Wq, ws, N, WO);
+  if constexpr (CPL > 0) {
+    if (K == ldk && ldk == 8 * CPL * 64 * WPR) {
+      launch_qr1<WPR, CPL, true>(grid, lds, s, X, M, K, ldk, vec, nwb, mb, Xq, xs, XO, n_out,
+                                 out_idx, Wq, ws, N, WO);
+      return;
+    }
+  }
+  launch_qr1<WPR, CPL, false>(grid, lds, s, X, M, K, ldk, vec, nwb, mb, Xq, xs, XO, n_out,
+                              out_idx, Wq, ws, N, WO);
 }
 
 hipError_t launch_quant_rows(const uint16_t* X, int M, int K, int ldk, const uint32_t* mask_bits,

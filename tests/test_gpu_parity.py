@@ -60,6 +60,14 @@ SHAPES = [
     (300, 4700, 64, 5, 6.0),       # row pass held in 10 chunks per lane (4 waves per SIMD)
     (280, 2600, 64, 3, 6.0),       # ... 6 chunks per lane
     (40, 10000, 64, 3, 6.0),       # a block per row, 6 chunks per lane
+    # rows of exactly the form's chunks (no per-chunk tests): a wave per row
+    # with 6, 12 and 16 chunks per lane, a block per row with 4, 6 and 8
+    (300, 3072, 64, 3, 6.0),
+    (264, 6144, 40, 2, 6.0),
+    (272, 8192, 64, 3, 6.0),
+    (100, 8192, 64, 3, 6.0),
+    (40, 12288, 64, 3, 6.0),
+    (20, 16384, 64, 2, 6.0),
     # more tiles than CUs with a short last round: its 14 tiles run as
     # 256x128 halves (one group of 8 pairs, 6 adjacent pairs), ragged in M
     # and N; then the same with more than three fp16 outlier steps (the

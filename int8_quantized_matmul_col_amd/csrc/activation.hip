@@ -187,6 +187,37 @@ __device__ int load_mask_prefix(const uint32_t* __restrict__ mask_bits, int nw,
   return total;
 }
 
+// The same prefix for mask words already in s_bits[], computed by wave 0
+// alone (each lane a run of consecutive words, one wave scan) and |O| handed
+// to every thread through LDS: one barrier, no cross-wave sums.  For the
+// 1024-thread single-launch decode pass, where the block-wide scan's
+// barriers and per-wave sums cost about a microsecond.
+template <int T>
+__device__ int mask_prefix_wave0(int nw, const uint32_t* s_bits, int* s_pre) {
+  __shared__ int s_total;
+  const int t = threadIdx.x, lane = t & 63;
+  if (t < 64) {
+    const int per = (nw + 63) / 64;
+    const int w0 = min(nw, lane * per), w1 = min(nw, w0 + per);
+    int local = 0;
+    for (int w = w0; w < w1; ++w) local += __popc(s_bits[w]);
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    int run = incl - local;
+    for (int w = w0; w < w1; ++w) {
+      s_pre[w] = run;
+      run += __popc(s_bits[w]);
+    }
+    if (lane == 63) s_total = incl;
+  }
+  __syncthreads();
+  return s_total;
+}
+
 // Column of the j-th outlier (0-based, j < |O|): the last word whose prefix is
 // <= j, then the (j - prefix)-th set bit in it.
 __device__ __forceinline__ int select_outlier(const uint32_t* s_bits, const int* s_pre, int nw,
@@ -644,9 +675,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // shared through L2) to form the column absmax and the mask itself, then
 // quantizes row m, which it kept in registers.  Workgroup 0 also writes the
 // mask words, |O| and the optional mask bytes and O list.  CPT = 8-column
-// chunks per thread (ldk <= T * 8 * CPT); rows are 16-byte aligned and
-// K % 8 == 0.  Dynamic LDS: 2*nw words.
-template <int CPT, int T>
+// chunks per thread (ldk <= T * 8 * CPT); MR = rows loaded per chunk (M <=
+// MR; rows past M repeat row M-1, so the MR loads are unconditional and in
+// flight together, and a single row costs one load, not sixteen: the
+// block's loads go through one CU's texture path); rows are 16-byte aligned
+// and K % 8 == 0.  Dynamic LDS: 2*nw words.
+template <int CPT, int T, int MR>
 __global__ __launch_bounds__(T) void k_activation_small(
     const uint16_t* __restrict__ X, int M, int K, int ldk, float threshold,
     uint8_t* __restrict__ mask8, uint32_t* __restrict__ mask_bits, int32_t* __restrict__ n_out,
@@ -670,14 +704,13 @@ __global__ __launch_bounds__(T) void k_activation_small(
     uint32_t mx[4] = {0u, 0u, 0u, 0u};  // |x| bits, two columns per word
     hv[u] = uint4{0u, 0u, 0u, 0u};
     if (c < nck) {
-      // rows past M repeat row M-1 (no effect on the max), so all 16 loads
-      // are unconditional and in flight together
-      uint4 rows[16];
+      // rows past M repeat row M-1 (no effect on the max)
+      uint4 rows[MR];
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < MR; ++r)
         rows[r] = reinterpret_cast<const uint4*>(X + (size_t)min(r, M - 1) * K)[c];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < MR; ++r) {
         mx[0] = pk_max_u16(mx[0], rows[r].x & 0x7fff7fffu);
         mx[1] = pk_max_u16(mx[1], rows[r].y & 0x7fff7fffu);
         mx[2] = pk_max_u16(mx[2], rows[r].z & 0x7fff7fffu);
@@ -698,7 +731,7 @@ __global__ __launch_bounds__(T) void k_activation_small(
     }
   }
   __syncthreads();
-  const int total = load_mask_prefix<T>(nullptr, nw, s_bits, s_pre);
+  const int total = mask_prefix_wave0<T>(nw, s_bits, s_pre);
   const int opad = (total + 63) & ~63;
 
   if (m == 0) {
@@ -866,10 +899,17 @@ hipError_t launch_activation_small(const uint16_t* X, int M, int K, int ldk, flo
   const size_t lds = (size_t)2 * (ldk / 32) * sizeof(uint32_t);
   // one thread per 8-column chunk where it fits: all the loads of a row in
   // one round (1024 threads up to 8192 columns, two chunks each beyond)
-#define AS(C, T) hipLaunchKernelGGL((k_activation_small<C, T>), dim3(M), dim3(T), lds, s, X, M, K, ldk, threshold, mask8, mask_bits, n_out, out_idx, Xq, x_scale, XO)
-  if (nch <= 256) AS(1, 256);
-  else if (nch <= 1024) AS(1, 1024);
-  else AS(2, 1024);
+#define AS(C, T, R) hipLaunchKernelGGL((k_activation_small<C, T, R>), dim3(M), dim3(T), lds, s, X, M, K, ldk, threshold, mask8, mask_bits, n_out, out_idx, Xq, x_scale, XO)
+#define AS_ROWS(C, T) \
+  if (M <= 1) AS(C, T, 1); else if (M <= 4) AS(C, T, 4); else AS(C, T, 16)
+  if (nch <= 256) {
+    AS_ROWS(1, 256);
+  } else if (nch <= 1024) {
+    AS_ROWS(1, 1024);
+  } else {
+    AS_ROWS(2, 1024);
+  }
+#undef AS_ROWS
 #undef AS
   return hipGetLastError();
 }

@@ -417,6 +417,10 @@ __device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restri
   Frag<TJ> f0, f1;
   prologue(lds, f0, p);
   run_steps<false, TJ>(lds, acc, f0, f1, p, 0, n8);
+  // step n8's sub-step-0 fragments are read again after the rescale (its
+  // stage is complete and nothing overwrites it before step n8 runs), so
+  // the fragment registers are free during it
+  f0 = Frag<TJ>{};
   // one column quad at a time (its scales and biases read once, applied to
   // the four row groups), so that few registers are live beside the
   // accumulators
@@ -438,6 +442,9 @@ __device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restri
               __float_as_int((float)acc[i][j][4 * q + e] * (sx[i] * w4[e]) + b4[e]);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+  for (int n = 0; n < TI + TJ; ++n)
+    fread1<TJ>(f0, lds, (uint32_t)(n8 & (NS - 1)) * kStage, p, 0, n);
   run_steps<true, TJ>(lds, acc, f0, f1, p, n8, n8 + nk16);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

@@ -1,6 +1,6 @@
 """Benchmark of the decomposed int8 matmul on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config sweep13b] [--extra q_proj,decode16]
+    python bench.py [--steps K] [--warmup W] [--config sweep13b] [--extra q_proj,decode1,decode16]
 
 One step = one whole int8_matmul call (activation pass: outlier detection,
 row quantization and compaction; int8 MFMA GEMM; fp16 outlier MFMA; fused
@@ -12,7 +12,7 @@ of 10 more calls against HBM bandwidth).  Prints one JSON line.
 * headline   -- the LLaMA-13B-shaped sweep workload at t = 6 (4096 tokens,
                5120 -> 13824), the largest single-GPU workload; ``extra``
                holds the same measurement, in the same process, for the 7B
-               q_proj prefill (4096^3) and the M = 16 decode call
+               q_proj prefill (4096^3) and the M = 1 and M = 16 decode calls
                (8192 -> 28672), so both halves of the metric (% int8 MFMA
                peak, % HBM bandwidth) are timed in one run.
 * value      -- effective TOPS = 2*M*N*K / (wall time of K steps / K).
@@ -566,7 +566,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="sweep13b")
-    ap.add_argument("--extra", default="q_proj,decode16",
+    ap.add_argument("--extra", default="q_proj,decode1,decode16",
                     help="workloads measured after the headline in the same run ('none': only "
                          "the headline)")
     ap.add_argument("--threshold", type=float, default=None)

@@ -140,6 +140,16 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
     return INT8MM_OK;
   }
 
+  // One row with only Y asked for: a single launch that codes X itself.
+  const bool stage_out = out.mask || out.n_outliers || out.outlier_idx || out.Xq ||
+                         out.x_scale || out.X_O || out.W_O || out.C;
+  if (L.decode && !stage_out && out.Y != nullptr && i8mm::gemm_decode_row_ok(X, m, k, ldk)) {
+    if ((e = i8mm::launch_gemm_decode_row(X, k, ldk, threshold, Wq, n, w_scale, bias, out.Y, s,
+                                          ev_start, ev_stop)) != hipSuccess)
+      return hip_fail(e);
+    return INT8MM_OK;
+  }
+
   uint32_t* bits = at<uint32_t>(ws, L.bits);
   int32_t* count = out.n_outliers ? out.n_outliers : at<int32_t>(ws, L.count);
   float* xs = out.x_scale ? out.x_scale : at<float>(ws, L.xscale);

@@ -174,4 +174,46 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, m);
 }
 
+// Bytes (or binary16 halves) of a chunk that belong to regular columns: the
+// mask bits ob (bit i = column i is an outlier) expanded to keep-masks.
+__device__ __forceinline__ uint32_t keep_bytes(uint32_t ob4) {
+  // bit i of ob4 (< 16) moved to bit 8i (the shifted copies do not overlap),
+  // then a byte permute turns each byte into 0x00 (bit set: selector 12) or
+  // 0xff (bit clear: selector 13); no full-width multiply
+  const uint32_t lsb = (ob4 * 0x00204081u) & 0x01010101u;
+  return __builtin_amdgcn_perm(0u, 0u, 0x0d0d0d0du - lsb);
+}
+// Clear-masks of the outlier columns of one 8-column chunk (mask bits ob,
+// bit i = column i), branch-free: v_perm's selectors 8 and 9 fill a byte
+// with bit 15 or bit 31 of its second source (10 and 11: of its first), so
+// with mask bits moved to bits 15 and 31 of shifted copies of ob, one permute
+// makes one mask word.  s3 holds bits 6 and 7 there, s2 bits 4 and 5, s1
+// bits 2 and 3, s0 bits 0 and 1 (no other bit of ob reaches 15 or 31).
+struct ChunkMasks {
+  uint32_t h[4];  // binary16 pair p: 0xffff over column 2p and/or 2p+1 if outliers
+  uint32_t b[2];  // code bytes 0-3 and 4-7: 0xff over each outlier column
+};
+__device__ __forceinline__ ChunkMasks chunk_masks(uint32_t ob) {
+  const uint32_t s3 = (ob << 9) | (ob << 24);
+  const uint32_t s2 = s3 << 2, s1 = s3 << 4, s0 = s3 << 6;
+  ChunkMasks m;
+  m.h[0] = __builtin_amdgcn_perm(0u, s0, 0x09090808u);
+  m.h[1] = __builtin_amdgcn_perm(0u, s1, 0x09090808u);
+  m.h[2] = __builtin_amdgcn_perm(0u, s2, 0x09090808u);
+  m.h[3] = __builtin_amdgcn_perm(0u, s3, 0x09090808u);
+  m.b[0] = __builtin_amdgcn_perm(s1, s0, 0x0b0a0908u);
+  m.b[1] = __builtin_amdgcn_perm(s3, s2, 0x0b0a0908u);
+  return m;
+}
+
+// Packed |x| maxima (two 16-bit lanes) of the regular columns of a chunk.
+__device__ __forceinline__ uint32_t chunk_absmax2(const uint4& w, const ChunkMasks& m) {
+  const uint32_t d0 = w.x & ~m.h[0] & 0x7fff7fffu, d1 = w.y & ~m.h[1] & 0x7fff7fffu;
+  const uint32_t d2 = w.z & ~m.h[2] & 0x7fff7fffu, d3 = w.w & ~m.h[3] & 0x7fff7fffu;
+  return pk_max_u16(pk_max_u16(d0, d1), pk_max_u16(d2, d3));
+}
+__device__ __forceinline__ uint32_t chunk_absmax2(const uint4& w, uint32_t ob) {
+  return chunk_absmax2(w, chunk_masks(ob));
+}
+
 }  // namespace i8mm

@@ -14,6 +14,16 @@
 // term; "PyTorch 2.9 supports LLM.int8()", section 3: merged at the end).
 // The 8 per-wave partials are summed in LDS in a fixed order (deterministic)
 // and the epilogue writes Y = fp16(fp32(C)*a_x*a_w/127^2 + Y_O).
+//
+// Every wave's first two K steps of weight are requested at kernel entry,
+// before the set-up (mask words, outlier-step scan, barriers), so the weight
+// stream starts with the kernel.  For a single row (M = 1) the column max is
+// the row's own |x|, so each workgroup can derive the mask, a_x and the codes
+// of X by itself (a 16 KiB row, read from L2 by all but the first
+// workgroups) while those loads are in flight: the whole call is one launch,
+// with the codes held in LDS ("PyTorch 2.9 supports LLM.int8()", section 2:
+// per-row absmax scale of the activations; "LLM.int8() notes", section 3.2:
+// outlier columns are those whose magnitude exceeds the threshold).
 #include "device_common.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -26,6 +36,10 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kU = 2;  // K steps per loop iteration
 constexpr int kSlots = 8;  // outlier K steps parked in LDS (more: static schedule)
 constexpr int kMaxWords = (133144 + 63) / 64 * 2;  // mask words for the largest K
+// single-row calls code X in the kernel up to this padded row length (its
+// codes are held in LDS beside the reduction and outlier-slot buffers)
+constexpr int kRowMaxLdk = 16384;
+constexpr int kRowChunks = kRowMaxLdk / 8 / kThreads;  // 8-column chunks per thread
 }  // namespace
 
 // A 16-byte Wq fragment.  The weight is read once per call and never again
@@ -35,15 +49,19 @@ __device__ __forceinline__ v4i wload(const int8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
 }
 
-template <int G, int MODE>  // MODE 0: Y, 1: int32 C
+// ROW: M == 1 and X coded here (Xq, x_scale and mask_bits unused); else the
+// codes, scales and mask words come from the activation pass.
+template <int G, int MODE, bool ROW>  // MODE 0: Y, 1: int32 C
 __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K, int ldk,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale,
-    const uint16_t* __restrict__ X, const uint32_t* __restrict__ mask_bits,
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ mask_bits, float threshold,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
-  __shared__ uint32_t s_bits[kMaxWords];
+  __shared__ uint32_t s_bits[ROW ? kRowMaxLdk / 32 : kMaxWords];
   __shared__ int s_red[kWaves][G * 256];
   __shared__ v4i s_wslot[kSlots][G][64];  // Wq fragments of the outlier steps
+  __shared__ v4i s_xq[ROW ? kRowMaxLdk / 16 : 1];  // ROW: the codes of X
+  __shared__ uint32_t s_wmax[kWaves];
   __shared__ int s_slot_step[kSlots];
   __shared__ int s_nslots;
   __shared__ int s_next;
@@ -51,12 +69,114 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nw = ldk / 32;
   const int nsteps = ldk / 64;
+
+  const int n_base = blockIdx.x * (G * 16);
+  const int ml = lane & 15;   // row of the Xq fragment / column of the result
+  const int kq = (lane >> 4) * 16;  // byte offset of this lane inside the 64-byte step
+
+  // panel-tiled operands (tile_layout.h): step s of row r is at
+  // tiled_offset(r, 64*s + kq) = tiled_offset(r, kq) + s * 16 KiB; the 16 rows
+  // of a group are 1 KiB contiguous per step
+  const int8_t* xrow = ROW ? nullptr : Xq + tiled_offset(ml, kq, ldk);
+  const bool xvalid = ml < M;
+  // The grid covers ceil(groups / G) * G groups of 16 rows, which can run past
+  // the prepared weight's padded rows when G does not divide the group count:
+  // such groups read the last padded row instead (their results are never
+  // stored, n >= N), so every load stays inside the weight.
+  const int row_cap = (int)padded_rows(N) - 1;
+  const int8_t* wrow[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    wrow[g] = Wq + tiled_offset(min(n_base + g * 16 + ml, row_cap), kq, ldk);
+
+  // Loads of the kU steps base .. base+kU-1 (steps past the last re-read the
+  // last one; their X fragments are zero, so they add nothing).
+  auto load_w = [&](int base, v4i (&b)[kU][G]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const size_t off = (size_t)min(base + u, nsteps - 1) * kTileBytes;
+#pragma unroll
+      for (int g = 0; g < G; ++g) b[u][g] = wload(wrow[g] + off);
+    }
+  };
+  auto load_x = [&](int base, v4i (&a)[kU]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int st = base + u;
+      if constexpr (ROW)
+        a[u] = (ml == 0 && st < nsteps) ? s_xq[(st * 64 + kq) >> 4] : v4i{};
+      else
+        a[u] = (xvalid && st < nsteps) ? *reinterpret_cast<const v4i*>(xrow + (size_t)st * kTileBytes)
+                                       : v4i{};
+    }
+  };
+
+  // wave w's first chunk: steps w*kU .. w*kU+kU-1, requested before the
+  // set-up.  (With 8 groups per workgroup the extra chunk would not fit the
+  // registers: there every step goes through the schedules below.)
+  constexpr bool kEarly = G <= 7;
+  const int first = kEarly ? wave * kU : ldk;
+  v4i b[kU][G];
+  v4i a[kU];
+  if constexpr (kEarly) {
+    load_w(first, b);
+    if constexpr (!ROW) load_x(first, a);
+  }
+
   if (t == 0) {
     s_nslots = 0;
-    s_next = 0;
+    s_next = kEarly ? kWaves * kU : 0;  // the dynamic schedule hands out the steps after the first chunks
   }
-  __syncthreads();
-  for (int w = t; w < nw; w += kThreads) s_bits[w] = mask_bits[w];
+  float ax = 0.0f;  // ROW: a_x of the row
+  if constexpr (ROW) {
+    // mask bytes (strict |x| > threshold; padding columns k >= K never), the
+    // absmax over the regular columns, then the codes of the row into LDS
+    const int nch = ldk / 8, nck = K >> 3;
+    uint8_t* s_ob = reinterpret_cast<uint8_t*>(s_bits);  // mask byte of chunk c
+    const uint4* xr = reinterpret_cast<const uint4*>(X);
+    uint4 hv[kRowChunks];
+    uint32_t ob[kRowChunks];
+#pragma unroll
+    for (int u = 0; u < kRowChunks; ++u) {
+      const int c = t + u * kThreads;
+      hv[u] = c < nck ? xr[c] : uint4{0u, 0u, 0u, 0u};
+    }
+    uint32_t mx2 = 0;
+#pragma unroll
+    for (int u = 0; u < kRowChunks; ++u) {
+      const int c = t + u * kThreads;
+      uint32_t o = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        o |= (h2f((uint16_t)habs_bits(half_at(hv[u], i))) > threshold ? 1u : 0u) << i;
+      ob[u] = o;
+      if (c < nch) s_ob[c] = (uint8_t)o;
+      mx2 = pk_max_u16(mx2, chunk_absmax2(hv[u], o));
+    }
+    const uint32_t mw = wave_max(max(mx2 & 0xffffu, mx2 >> 16));
+    if (lane == 0) s_wmax[wave] = mw;
+    __syncthreads();
+    uint32_t mx = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = max(mx, s_wmax[w]);
+    ax = h2f((uint16_t)mx);
+    const float r = ax == 0.0f ? 0.0f : 127.0f / ax;
+    uint2* s_xq2 = reinterpret_cast<uint2*>(s_xq);
+#pragma unroll
+    for (int u = 0; u < kRowChunks; ++u) {
+      const int c = t + u * kThreads;
+      if (c < nch) {
+        float dev;
+        uint2 q = quant8_fast(hv[u], r, &dev);
+        if (dev > kTieGuard) q = quant8_exact(hv[u], ax);
+        q.x &= keep_bytes(ob[u] & 0xfu);
+        q.y &= keep_bytes(ob[u] >> 4);
+        s_xq2[c] = q;
+      }
+    }
+  } else {
+    for (int w = t; w < nw; w += kThreads) s_bits[w] = mask_bits[w];
+  }
   __syncthreads();
   // K steps holding outlier columns, in ascending order (one wave, ballots)
   if (wave == 0) {
@@ -74,32 +194,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   __syncthreads();
   const int n_oslots = s_nslots;
   const bool has_outliers = n_oslots > 0;
-  // Few outlier steps: the int8 work is handed out dynamically (the waves of
-  // a workgroup finish together instead of the slowest setting the pace) and
-  // the outlier steps' Wq fragments are parked in LDS for a fixed-order fp16
-  // pass at the end (the result stays deterministic).  Many: static split
-  // with the outlier term inline.
+  // Few outlier steps: the int8 work after the first chunks is handed out
+  // dynamically (the waves of a workgroup finish together instead of the
+  // slowest setting the pace) and the outlier steps' Wq fragments are parked
+  // in LDS for a fixed-order fp16 pass at the end (the result stays
+  // deterministic).  Many: static split with the outlier term inline.
   const bool dynamic = n_oslots <= kSlots;
-
-  const int n_base = blockIdx.x * (G * 16);
-  const int s0 = (nsteps * wave) / kWaves, s1 = (nsteps * (wave + 1)) / kWaves;
-  const int ml = lane & 15;   // row of the Xq fragment / column of the result
-  const int kq = (lane >> 4) * 16;  // byte offset of this lane inside the 64-byte step
-
-  // panel-tiled operands (tile_layout.h): step s of row r is at
-  // tiled_offset(r, 64*s + kq) = tiled_offset(r, kq) + s * 16 KiB; the 16 rows
-  // of a group are 1 KiB contiguous per step
-  const int8_t* xrow = Xq + tiled_offset(ml, kq, ldk);
-  const bool xvalid = ml < M;
-  // The grid covers ceil(groups / G) * G groups of 16 rows, which can run past
-  // the prepared weight's padded rows when G does not divide the group count:
-  // such groups read the last padded row instead (their results are never
-  // stored, n >= N), so every load stays inside the weight.
-  const int row_cap = (int)padded_rows(N) - 1;
-  const int8_t* wrow[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-    wrow[g] = Wq + tiled_offset(min(n_base + g * 16 + ml, row_cap), kq, ldk);
 
   v4i acc[G];
   v4f acco[G];
@@ -109,16 +209,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     acco[g] = v4f{};
   }
 
-  // fp16 outlier term of step s for this lane's 16 columns k0 .. k0+15 (b:
+  // fp16 outlier term of step s for this lane's 16 columns k0 .. k0+15 (bw:
   // the step's Wq fragments, already in registers)
-  auto outlier_step = [&](int s, const v4i (&b)[G]) {
+  auto outlier_step = [&](int s, const v4i (&bw)[G]) __attribute__((always_inline)) {
     const int k0 = s * 64 + kq;
-    const uint32_t ob = (s_bits[k0 >> 5] >> (k0 & 31)) & 0xffffu;
+    const uint32_t obits = (s_bits[k0 >> 5] >> (k0 & 31)) & 0xffffu;
     v8h xa[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       uint16_t v = 0;
-      if (((ob >> e) & 1u) && xvalid) v = X[(size_t)ml * K + k0 + e];
+      if (((obits >> e) & 1u) && xvalid) v = X[(size_t)ml * K + k0 + e];
       xa[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
     }
 #pragma unroll
@@ -129,8 +229,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         uint16_t v = 0;
-        if ((ob >> e) & 1u) {
-          const int q = (int)(int8_t)((b[g][e >> 2] >> ((e & 3) * 8)) & 0xff);
+        if ((obits >> e) & 1u) {
+          const int q = (int)(int8_t)((bw[g][e >> 2] >> ((e & 3) * 8)) & 0xff);
           v = dequant_w_half(q, aw);
         }
         wb[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
@@ -141,6 +241,44 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   };
   auto step_has_outliers = [&](int s) { return (s_bits[2 * s] | s_bits[2 * s + 1]) != 0u; };
 
+  // MFMAs of a loaded chunk; its outlier steps parked in their LDS slots
+  // (dynamic schedule) or accumulated at once (static)
+  auto mfma_chunk = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][g], acc[g], 0, 0, 0);
+  };
+  auto park_chunk = [&](int base) __attribute__((always_inline)) {
+    if (!has_outliers) return;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int st = min(base + u, nsteps - 1);
+      if (base + u < nsteps && step_has_outliers(st)) {
+        int k = 0;
+        while (s_slot_step[k] != st) ++k;  // present: at most kSlots entries
+#pragma unroll
+        for (int g = 0; g < G; ++g) s_wslot[k][g][lane] = b[u][g];
+      }
+    }
+  };
+  auto inline_chunk = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int st = min(base + u, nsteps - 1);
+      if (base + u < nsteps && step_has_outliers(st)) outlier_step(st, b[u]);
+    }
+  };
+
+  // The prefetched chunk.  In the static schedule its outlier steps come at
+  // the end, their weight fragments read a second time (many outlier steps
+  // only: at most kU of them per wave).
+  if (kEarly && first < nsteps) {
+    if constexpr (ROW) load_x(first, a);
+    mfma_chunk();
+    if (dynamic) park_chunk(first);
+  }
   if (dynamic) {
     // chunks of kU steps from a workgroup counter, fetched one chunk ahead
     int base = 0;
@@ -149,75 +287,54 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     while (base < nsteps) {
       int nb = 0;
       if (lane == 0) nb = atomicAdd(&s_next, kU);
-      v4i b[kU][G];
-      v4i a[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int sl = min(base + u, nsteps - 1);  // a short last chunk re-reads, not counted
-        const size_t off = (size_t)sl * kTileBytes;
-#pragma unroll
-        for (int g = 0; g < G; ++g) b[u][g] = wload(wrow[g] + off);
-        a[u] = (xvalid && base + u < nsteps) ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][g], acc[g], 0, 0, 0);
-      if (has_outliers) {
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int st = min(base + u, nsteps - 1);
-          if (base + u < nsteps && step_has_outliers(st)) {
-            int k = 0;
-            while (s_slot_step[k] != st) ++k;  // present: at most kSlots entries
-#pragma unroll
-            for (int g = 0; g < G; ++g) s_wslot[k][g][lane] = b[u][g];
-          }
-        }
-      }
+      load_w(base, b);
+      load_x(base, a);
+      mfma_chunk();
+      park_chunk(base);
       base = __builtin_amdgcn_readfirstlane(nb);
     }
     __syncthreads();
     // fp16 outlier term, slot k on wave k % kWaves, in slot order
     for (int k = wave; k < n_oslots; k += kWaves) {
-      v4i b[G];
+      v4i bw[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) b[g] = s_wslot[k][g][lane];
-      outlier_step(s_slot_step[k], b);
+      for (int g = 0; g < G; ++g) bw[g] = s_wslot[k][g][lane];
+      outlier_step(s_slot_step[k], bw);
     }
   } else {
-    // kU steps per iteration: all their loads are issued before the first
-    // MFMA, so a wave keeps kU*G KiB of weight reads in flight
+    // the steps after the first chunks split evenly over the waves, kU per
+    // iteration: all their loads are issued before the first MFMA, so a
+    // wave keeps kU*G KiB of weight reads in flight
+    const int done = kEarly ? min(kWaves * kU, nsteps) : 0;
+    const int s0 = done + ((nsteps - done) * wave) / kWaves;
+    const int s1 = done + ((nsteps - done) * (wave + 1)) / kWaves;
     int s = s0;
     for (; s + kU <= s1; s += kU) {
-      v4i b[kU][G];
-      v4i a[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const size_t off = (size_t)(s + u) * kTileBytes;
-#pragma unroll
-        for (int g = 0; g < G; ++g) b[u][g] = wload(wrow[g] + off);
-        a[u] = xvalid ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u][g], acc[g], 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-        if (step_has_outliers((s + u))) outlier_step((s + u), b[u]);
+      load_w(s, b);
+      load_x(s, a);
+      mfma_chunk();
+      inline_chunk(s);
     }
     for (; s < s1; ++s) {
       const size_t off = (size_t)s * kTileBytes;
-      v4i b[G];
+      v4i bw[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) b[g] = wload(wrow[g] + off);
-      const v4i a = xvalid ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
+      for (int g = 0; g < G; ++g) bw[g] = wload(wrow[g] + off);
+      v4i xa1;
+      if constexpr (ROW)
+        xa1 = ml == 0 ? s_xq[(s * 64 + kq) >> 4] : v4i{};
+      else
+        xa1 = xvalid ? *reinterpret_cast<const v4i*>(xrow + off) : v4i{};
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[g], acc[g], 0, 0, 0);
-      if (step_has_outliers(s)) outlier_step(s, b);
+      for (int g = 0; g < G; ++g) acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa1, bw[g], acc[g], 0, 0, 0);
+      if (step_has_outliers(s)) outlier_step(s, bw);
+    }
+    for (int st = first; st < min(first + kU, nsteps); ++st) {
+      if (!step_has_outliers(st)) continue;
+      v4i bw[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) bw[g] = wload(wrow[g] + (size_t)st * kTileBytes);
+      outlier_step(st, bw);
     }
   }
 
@@ -273,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     if (MODE == 1) {
       C[(size_t)m * N + n] = csum[u];
     } else {
-      const float sc = x_scale[m] * w_scale[n] * kInv127Sq;
+      const float sc = (ROW ? ax : x_scale[m]) * w_scale[n] * kInv127Sq;
       const float b = bias != nullptr ? h2f(bias[n]) : 0.0f;
       Y[(size_t)m * N + n] = f2h((float)csum[u] * sc + osum[u] + b);
     }
@@ -283,36 +400,74 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
 template <int G>
 static void launch_g(dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1, const int8_t* Xq, const int8_t* Wq, int M, int N,
                      int K, int ldk, const float* xs, const float* ws, const uint16_t* X,
-                     const uint32_t* mb, const uint16_t* bias, uint16_t* Y, int32_t* C) {
-  if (C != nullptr)
-    hipExtLaunchKernelGGL((k_gemm_decode<G, 1>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq, Wq, M,
-                          N, K, ldk, xs, ws, X, mb, bias, Y, C);
+                     const uint32_t* mb, float threshold, const uint16_t* bias, uint16_t* Y,
+                     int32_t* C) {
+  if (Xq == nullptr)
+    hipExtLaunchKernelGGL((k_gemm_decode<G, 0, true>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
+                          Wq, M, N, K, ldk, xs, ws, X, mb, threshold, bias, Y, C);
+  else if (C != nullptr)
+    hipExtLaunchKernelGGL((k_gemm_decode<G, 1, false>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
+                          Wq, M, N, K, ldk, xs, ws, X, mb, threshold, bias, Y, C);
   else
-    hipExtLaunchKernelGGL((k_gemm_decode<G, 0>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq, Wq, M,
-                          N, K, ldk, xs, ws, X, mb, bias, Y, C);
+    hipExtLaunchKernelGGL((k_gemm_decode<G, 0, false>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
+                          Wq, M, N, K, ldk, xs, ws, X, mb, threshold, bias, Y, C);
 }
 
-hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
-                              const float* x_scale, const float* w_scale, const uint16_t* X,
-                              const uint32_t* mask_bits, const uint16_t* bias, uint16_t* Y,
-                              int32_t* C, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+// Xq == nullptr: the single-row form that codes X itself (M == 1, Y output).
+static hipError_t launch_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
+                                const float* x_scale, const float* w_scale, const uint16_t* X,
+                                const uint32_t* mask_bits, float threshold, const uint16_t* bias,
+                                uint16_t* Y, int32_t* C, hipStream_t s, hipEvent_t e0,
+                                hipEvent_t e1) {
   // Spread the 16-row groups evenly over the 256 CUs: G groups per workgroup.
   const int groups = (N + 15) / 16;
   int G = (groups + 255) / 256;
   if (G > 8) G = 8;
   if (G < 1) G = 1;
   dim3 grid((groups + G - 1) / G);
+#define I8MM_DECODE_G(g)                                                                  \
+  case g:                                                                                 \
+    launch_g<g>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, \
+                threshold, bias, Y, C);                                                   \
+    break;
   switch (G) {
-    case 1: launch_g<1>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
-    case 2: launch_g<2>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
-    case 3: launch_g<3>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
-    case 4: launch_g<4>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
-    case 5: launch_g<5>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
-    case 6: launch_g<6>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
-    case 7: launch_g<7>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
-    default: launch_g<8>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, bias, Y, C); break;
+    I8MM_DECODE_G(1)
+    I8MM_DECODE_G(2)
+    I8MM_DECODE_G(3)
+    I8MM_DECODE_G(4)
+    I8MM_DECODE_G(5)
+    I8MM_DECODE_G(6)
+    I8MM_DECODE_G(7)
+    default:
+      launch_g<8>(grid, s, e0, e1, Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits,
+                  threshold, bias, Y, C);
+      break;
   }
+#undef I8MM_DECODE_G
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
+                              const float* x_scale, const float* w_scale, const uint16_t* X,
+                              const uint32_t* mask_bits, const uint16_t* bias, uint16_t* Y,
+                              int32_t* C, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (Xq == nullptr) return hipErrorInvalidValue;
+  return launch_decode(Xq, Wq, M, N, K, ldk, x_scale, w_scale, X, mask_bits, 0.0f, bias, Y, C,
+                       s, e0, e1);
+}
+
+bool gemm_decode_row_ok(const uint16_t* X, int M, int K, int ldk) {
+  return M == 1 && K > 0 && (K % 8) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 &&
+         ldk <= kRowMaxLdk;
+}
+
+hipError_t launch_gemm_decode_row(const uint16_t* X, int K, int ldk, float threshold,
+                                  const int8_t* Wq, int N, const float* w_scale,
+                                  const uint16_t* bias, uint16_t* Y, hipStream_t s, hipEvent_t e0,
+                                  hipEvent_t e1) {
+  if (!gemm_decode_row_ok(X, 1, K, ldk) || Y == nullptr) return hipErrorInvalidValue;
+  return launch_decode(nullptr, Wq, 1, N, K, ldk, nullptr, w_scale, X, nullptr, threshold, bias,
+                       Y, nullptr, s, e0, e1);
 }
 
 }  // namespace i8mm

@@ -103,4 +103,10 @@ def run_case(mm, X16, W16, t, stages=True, repeat=2):
     check_y(Y, Y_ref, X16, Wq_r, s_r, st["O"].size)
     for Y2 in Ys[1:]:
         assert np.array_equal(Y2.cpu().numpy().view(np.uint16), Y.view(np.uint16)), "nondeterministic Y"
+    if X16.shape[0] == 1:
+        # one row: int8_matmul codes X inside the decode kernel; the stage
+        # call takes the activation launch, whose codes were checked above
+        Ys = mm.int8_matmul_stages(X_d, Wq_d, s_d, threshold=t, want_c=False)["Y"]
+        torch.cuda.synchronize()
+        assert np.array_equal(Ys.cpu().numpy().view(np.uint16), Y.view(np.uint16)), "one-row Y"
     return Y, Y_ref

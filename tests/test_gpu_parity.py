@@ -44,6 +44,14 @@ SHAPES = [
     (1, 1024, 8704, 3, 6.0),
     (16, 1024, 8704, 3, 6.0),
     (16, 4096, 11008, 4, 6.0),
+    # one row (M = 1): the decode kernel codes X itself up to ldk = 16384 --
+    # many outlier steps (its static schedule), t = 0 (a_x = 0), t = inf,
+    # 2049 groups of 16 rows (8 per workgroup); past 16384 the activation launch
+    (1, 2048, 300, 40, 6.0),
+    (1, 520, 100, 4, 0.0),
+    (1, 200, 33, 3, math.inf),
+    (1, 512, 32784, 3, 6.0),
+    (1, 16392, 40, 2, 6.0),
     # prefill path: M > 16
     (17, 1024, 1024, 2, 6.0),
     (300, 520, 300, 5, 6.0),
@@ -92,6 +100,8 @@ def test_threshold_equal_to_column_max_is_not_outlier(lib):
     X[:, 30] = np.float16(-6.0)
     for M in (40, 8):
         Y, _ = run_case(lib, X[:M].copy(), W, 6.0)
+    for r in (7, 3):  # one row holding the column max (M = 1)
+        run_case(lib, X[r:r + 1].copy(), W, 6.0)
 
 
 def test_zero_rows_and_columns(lib):
@@ -106,6 +116,9 @@ def test_zero_rows_and_columns(lib):
     X2[6] = 0
     X2[6, 3] = 50.0
     run_case(lib, X2, W, 6.0)
+    # the same rows alone (M = 1: coded inside the decode kernel)
+    run_case(lib, X[5:6].copy(), W, 6.0)
+    run_case(lib, X2[6:7].copy(), W, 6.0)
 
 
 def test_exact_ties_round_half_even(lib):
@@ -120,7 +133,7 @@ def test_exact_ties_round_half_even(lib):
     W = np.clip(W, -3.96875, 3.96875)
     W[:, 1] = -3.96875
     W = W.astype(np.float16)
-    for m in (M, 7):
+    for m in (M, 7, 1):
         run_case(lib, X[:m].copy(), W, 6.0)
 
 

@@ -44,14 +44,20 @@ SHAPES = [
     (1, 1024, 8704, 3, 6.0),
     (16, 1024, 8704, 3, 6.0),
     (16, 4096, 11008, 4, 6.0),
-    # one row (M = 1): the decode kernel codes X itself up to ldk = 16384 --
-    # many outlier steps (its static schedule), t = 0 (a_x = 0), t = inf,
-    # 2049 groups of 16 rows (8 per workgroup); past 16384 the activation launch
+    # one row: the decode kernel codes X itself up to ldk = 16384 -- many
+    # outlier steps (its static schedule), t = 0 (a_x = 0), t = inf, 2049
+    # groups of 16 rows (8 per workgroup); past 16384 the activation launch.
+    # The same cases at two to four rows (activation launch, then decode).
     (1, 2048, 300, 40, 6.0),
     (1, 520, 100, 4, 0.0),
     (1, 200, 33, 3, math.inf),
     (1, 512, 32784, 3, 6.0),
     (1, 16392, 40, 2, 6.0),
+    (2, 8192, 300, 40, 6.0),
+    (4, 520, 100, 4, 0.0),
+    (2, 200, 33, 3, math.inf),
+    (4, 512, 32784, 3, 6.0),
+    (3, 8200, 64, 3, 6.0),
     # prefill path: M > 16
     (17, 1024, 1024, 2, 6.0),
     (300, 520, 300, 5, 6.0),
@@ -116,9 +122,10 @@ def test_zero_rows_and_columns(lib):
     X2[6] = 0
     X2[6, 3] = 50.0
     run_case(lib, X2, W, 6.0)
-    # the same rows alone (M = 1: coded inside the decode kernel)
+    # the same rows alone (coded inside the decode kernel) and among four
     run_case(lib, X[5:6].copy(), W, 6.0)
     run_case(lib, X2[6:7].copy(), W, 6.0)
+    run_case(lib, X2[4:8].copy(), W, 6.0)
 
 
 def test_exact_ties_round_half_even(lib):

@@ -469,7 +469,7 @@ __device__ __forceinline__ void gemm_tile_many(char* lds, const int8_t* __restri
 // step that targeted it fetched nothing) and stages Y (8 KiB per wave).  Per
 // 32-row group i: Y = fp32(C)*s + b straight from the int32 accumulators,
 // the outlier products accumulated on top, fp16 rows stored.
-template <int TJ, bool INTERIOR>
+template <int TJ, bool INTERIOR, bool OUTLIERS>
 __device__ __forceinline__ void epilogue_few(char* lds, v16i (&acc)[TI][TJ], const Pipe& p, int nr,
                                              int nk16, char* ys, uint16_t* __restrict__ Y, int M,
                                              int N, int m0, int n0, bool vec) {
@@ -502,7 +502,12 @@ __device__ __forceinline__ void epilogue_few(char* lds, v16i (&acc)[TI][TJ], con
           acc[i][j][4 * q + e] =
               __float_as_int((float)acc[i][j][4 * q + e] * (sx * w4[e]) + b4[e]);
       }
-    for (int st = 0; st < nk16; ++st) {
+    // at least one step when OUTLIERS (tiles without outlier steps take the
+    // form without the loop: a loop that may run no times makes the compiler
+    // copy the rescaled group into the MFMA registers twice)
+    if constexpr (OUTLIERS) {
+    int st = 0;
+    do {
       const uint32_t sb = (uint32_t)((nr + st) & (NS - 1)) * kStage;
       // all of the step's fragments first, so the reads overlap instead of
       // each MFMA waiting on the one read before it
@@ -522,6 +527,7 @@ __device__ __forceinline__ void epilogue_few(char* lds, v16i (&acc)[TI][TJ], con
               v16i, __builtin_amdgcn_mfma_f32_32x32x16_f16(
                         __builtin_bit_cast(v8h, bb[kk][j]), __builtin_bit_cast(v8h, a[kk]),
                         __builtin_bit_cast(v16f, acc[i][j]), 0, 0, 0));
+    } while (++st < nk16);
     }
     v16f y[TJ];
 #pragma unroll
@@ -583,10 +589,17 @@ __device__ __forceinline__ void tile_work(char* lds, const int8_t* __restrict__ 
   char* ys = lds + ((nr + NS - 1) & (NS - 1)) * kStage + wave * 8192;
   // a uniform branch: tiles wholly inside Y (all but the ragged edge) store
   // without checks
-  if (vec && m0 + BM <= M && n0 + 64 * TJ <= N)
-    epilogue_few<TJ, true>(lds, acc, p, nr, nk16, ys, Y, M, N, m0, n0, vec);
-  else
-    epilogue_few<TJ, false>(lds, acc, p, nr, nk16, ys, Y, M, N, m0, n0, vec);
+  if (vec && m0 + BM <= M && n0 + 64 * TJ <= N) {
+    if (nk16 > 0)
+      epilogue_few<TJ, true, true>(lds, acc, p, nr, nk16, ys, Y, M, N, m0, n0, vec);
+    else
+      epilogue_few<TJ, true, false>(lds, acc, p, nr, nk16, ys, Y, M, N, m0, n0, vec);
+  } else {
+    if (nk16 > 0)
+      epilogue_few<TJ, false, true>(lds, acc, p, nr, nk16, ys, Y, M, N, m0, n0, vec);
+    else
+      epilogue_few<TJ, false, false>(lds, acc, p, nr, nk16, ys, Y, M, N, m0, n0, vec);
+  }
 }
 
 }  // namespace

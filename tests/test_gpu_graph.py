@@ -17,7 +17,9 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("M,K,N,with_bias", [(300, 1024, 512, False), (300, 1024, 512, True),
                                              (300, 2112, 520, True),  # every tile as two halves
-                                             (8, 2048, 1024, False), (8, 2048, 1024, True)])
+                                             (8, 2048, 1024, False), (8, 2048, 1024, True),
+                                             # one row: the decode kernel codes X itself
+                                             (1, 2048, 1024, False), (1, 2048, 1024, True)])
 def test_graph_replay_matches_eager(lib, M, K, N, with_bias):
     import torch
     print(f"case graph M={M} K={K} N={N} bias={with_bias}", flush=True)

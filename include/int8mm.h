@@ -201,6 +201,32 @@ INT8MM_API int int8_column_absmax(const int8mm_half* X, int64_t M, int64_t K,
                        hipStream_t stream);
 
 /*
+ * int8_outlier_counts -- |O| at several thresholds from the column maxima:
+ * counts[i] = number of columns k < K with colmax[k] > thresholds[i], the
+ * strict comparison of the outlier test (binary16 maximum widened to fp32).
+ * What each candidate threshold would send to the fp16 path ("LLM.int8()
+ * notes", section 5.1: set the threshold from the activations' statistics;
+ * section 2.3: a low threshold moves many columns to fp16, a high one
+ * quantizes the outliers).
+ *
+ *   colmax      [K]            float16 device pointer (e.g. from
+ *                              int8_column_absmax); may be NULL when K == 0.
+ *   thresholds  [n_thresholds] float HOST pointer, each >= 0 (+inf allowed),
+ *                              copied into the launch (the caller may reuse
+ *                              the array as soon as the call returns).
+ *   n_thresholds               1 .. INT8MM_MAX_COUNT_THRESHOLDS.
+ *   counts      [n_thresholds] int32 device pointer, out.
+ * K == 0: every count is 0.  Errors: EINVAL (null thresholds or counts; null
+ * colmax with K > 0; n_thresholds out of range; a NaN or negative
+ * threshold; misaligned colmax or counts), ESHAPE (K < 0 or > INT8MM_MAX_K),
+ * EHIP.  All checks run before anything is enqueued.
+ */
+#define INT8MM_MAX_COUNT_THRESHOLDS 64
+
+INT8MM_API int int8_outlier_counts(const int8mm_half* colmax, int64_t K, const float* thresholds,
+                                   int n_thresholds, int32_t* counts, hipStream_t stream);
+
+/*
  * int8_matmul_stages -- the same kernels as int8_matmul for this shape, with
  * every intermediate of the method exposed (for verification).  Every output
  * pointer is optional (NULL = not wanted).  When C is given the matmul kernel

@@ -14,7 +14,8 @@ Python binding over it, with torch used only for device memory and streams.
 ``Int8Linear`` wraps the same calls as a torch module (forward only), and
 ``replace_linear_with_int8`` swaps the fp16 ``nn.Linear`` layers of a model
 for it.  ``outlier_stats`` summarizes the column maxima of an activation
-(``int8_column_absmax``) to help choose the threshold.
+(``int8_column_absmax``) and |O| at candidate thresholds
+(``int8_outlier_counts``) to help choose the threshold.
 """
 
 from .binding import (  # noqa: F401
@@ -30,6 +31,7 @@ from .binding import (  # noqa: F401
     int8_matmul_profiled,
     int8_matmul_stages,
     int8_matmul_workspace_size,
+    int8_outlier_counts,
     int8_pack_weight,
     int8_prepare_weight,
     int8_weight_bytes,

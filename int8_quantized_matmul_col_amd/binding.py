@@ -26,6 +26,7 @@ INT8MM_EHIP = -4
 INT8MM_ESCRATCH = -5
 INT8MM_MAX_K = 133144
 INT8MM_DECODE_MAX_M = 16
+INT8MM_MAX_COUNT_THRESHOLDS = 64
 
 # Default outlier threshold (the value of the pages' 8-bit loading config).
 DEFAULT_THRESHOLD = 6.0
@@ -46,6 +47,7 @@ SIGNATURES = {
     "int8_matmul_profiled": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P,
                                             ctypes.c_size_t, _P, _P, _P]),
     "int8_column_absmax": (ctypes.c_int, [_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "int8_outlier_counts": (ctypes.c_int, [_P, _I64, _P, ctypes.c_int, _P, _P]),
     "int8_matmul_stages": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float,
                                           _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, ctypes.c_size_t, _P]),
@@ -318,6 +320,29 @@ def int8_column_absmax(X, out=None, workspace=None):
                                 _stream(dev))
     _check("int8_column_absmax", st)
     return cm
+
+
+def int8_outlier_counts(colmax, thresholds, out=None):
+    """counts[i] = number of columns with colmax[k] > thresholds[i] (int32
+    [len(thresholds)] on colmax's device): |O| at each threshold, counted on
+    the GPU with the outlier test's own comparison.  colmax float16 [K] (from
+    int8_column_absmax); at most INT8MM_MAX_COUNT_THRESHOLDS thresholds, each
+    >= 0 (+inf allowed)."""
+    import torch
+    lib = load()
+    _require(colmax, torch.float16, "colmax")
+    if colmax.dim() != 1:
+        raise ValueError("colmax must be 1-D [K]")
+    ts = [float(t) for t in thresholds]
+    n = len(ts)
+    dev = colmax.device
+    counts = out if out is not None else torch.empty((n,), dtype=torch.int32, device=dev)
+    if out is not None:
+        _check_out(counts, (n,), torch.int32, "out", dev)
+    arr = (ctypes.c_float * max(n, 1))(*ts)
+    st = lib.int8_outlier_counts(_ptr(colmax), colmax.numel(), arr, n, _ptr(counts), _stream(dev))
+    _check("int8_outlier_counts", st)
+    return counts
 
 
 def int8_matmul_profiled(X, Wq, w_scale, threshold: float, out, workspace, ev_start: int,

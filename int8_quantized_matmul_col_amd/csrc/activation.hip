@@ -738,6 +738,33 @@ __global__ __launch_bounds__(T) void k_activation_small(
   if (t == 0) x_scale[m] = a;
 }
 
+// counts[i] = number of columns k < K with colmax[k] > thr.t[i]: |O| at each
+// threshold, with the comparison k_colmask makes (binary16 maximum widened
+// to fp32, strict).  One workgroup per threshold; four independent loads
+// per thread and round.
+__global__ __launch_bounds__(256) void k_count_above(const uint16_t* __restrict__ colmax, int K,
+                                                     CountThresholds thr,
+                                                     int32_t* __restrict__ counts) {
+  const float t = thr.t[blockIdx.x];
+  int c = 0;
+  for (int k0 = (int)threadIdx.x; k0 < K; k0 += 4 * 256) {
+    uint16_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u * 256;
+      v[u] = k < K ? colmax[k] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c += (k0 + u * 256 < K && h2f(v[u]) > t) ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  __shared__ int s[4];
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) counts[blockIdx.x] = s[0] + s[1] + s[2] + s[3];
+}
+
 __global__ void k_zero_half(uint16_t* __restrict__ Y, int64_t count) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -878,6 +905,13 @@ hipError_t launch_bias_rows(const uint16_t* bias, int64_t M, int64_t N, uint16_t
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_bias_rows, dim3((unsigned)blocks), dim3(256), 0, s, bias, M, N, Y);
+  return hipGetLastError();
+}
+
+hipError_t launch_count_above(const uint16_t* colmax, int K, const CountThresholds& thr, int n,
+                              int32_t* counts, hipStream_t s) {
+  if (n < 1 || n > kMaxCountThresholds || K < 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_count_above, dim3(n), dim3(256), 0, s, colmax, K, thr, counts);
   return hipGetLastError();
 }
 

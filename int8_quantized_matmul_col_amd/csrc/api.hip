@@ -12,6 +12,9 @@
 #include "launch.h"
 #include "tile_layout.h"
 
+static_assert(INT8MM_MAX_COUNT_THRESHOLDS == i8mm::kMaxCountThresholds,
+              "threshold count limit of the header and the kernel");
+
 namespace {
 
 thread_local char g_hip_error[256] = "";
@@ -285,6 +288,23 @@ INT8MM_API int int8_column_absmax(const int8mm_half* X, int64_t M, int64_t K,
   if ((e = i8mm::launch_colmask(X, part, L.rc, m, k, ldk, INFINITY, nullptr, bits, stream,
                                 colmax)) != hipSuccess)
     return hip_fail(e);
+  return INT8MM_OK;
+}
+
+INT8MM_API int int8_outlier_counts(const int8mm_half* colmax, int64_t K, const float* thresholds,
+                                   int n_thresholds, int32_t* counts, hipStream_t stream) {
+  if (K < 0 || K > INT8MM_MAX_K) return INT8MM_ESHAPE;
+  if (thresholds == nullptr || counts == nullptr || (K > 0 && colmax == nullptr))
+    return INT8MM_EINVAL;
+  if (n_thresholds < 1 || n_thresholds > INT8MM_MAX_COUNT_THRESHOLDS) return INT8MM_EINVAL;
+  if (!aligned(colmax, 2) || !aligned(counts, 4)) return INT8MM_EINVAL;
+  i8mm::CountThresholds thr{};
+  for (int i = 0; i < n_thresholds; ++i) {
+    if (isnan(thresholds[i]) || thresholds[i] < 0.0f) return INT8MM_EINVAL;
+    thr.t[i] = thresholds[i];
+  }
+  hipError_t e = i8mm::launch_count_above(colmax, (int)K, thr, n_thresholds, counts, stream);
+  if (e != hipSuccess) return hip_fail(e);
   return INT8MM_OK;
 }
 

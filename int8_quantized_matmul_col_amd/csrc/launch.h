@@ -65,6 +65,14 @@ hipError_t launch_gemm_decode_row(const uint16_t* X, int K, int ldk, float thres
                                   hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // Y[0 .. count) = 0 (K == 0 case).
 hipError_t launch_zero_half(uint16_t* Y, int64_t count, hipStream_t s);
+// Thresholds of one int8_outlier_counts call, passed by value (kernel
+// arguments): at most kMaxCountThresholds of them.
+constexpr int kMaxCountThresholds = 64;
+struct CountThresholds {
+  float t[kMaxCountThresholds];
+};
+hipError_t launch_count_above(const uint16_t* colmax, int K, const CountThresholds& thr, int n,
+                              int32_t* counts, hipStream_t s);
 // Y[m][n] = bias[n] for an [M][N] Y (K == 0 case with a bias).
 hipError_t launch_bias_rows(const uint16_t* bias, int64_t M, int64_t N, uint16_t* Y,
                             hipStream_t s);

@@ -9,11 +9,11 @@ too high a one quantizes the outliers (accuracy collapses).
 
 What decides the split is the per-column maximum colmax[k] = max_m |X[m,k]|:
 column k is an outlier column for every threshold t < colmax[k].  It comes
-from the library's outlier-detection kernels (``int8_column_absmax``, exact).
-The summaries below are tool logic, not a step of the matmul path: small
-torch reductions over those K values (counts of colmax > t, a percentile)
-that report what each candidate threshold would send to fp16.  The path's
-own comparison with the threshold is done inside the library's kernels.
+from the library's outlier-detection kernels (``int8_column_absmax``, exact),
+and |O| at each candidate threshold is counted by the library as well
+(``int8_outlier_counts``, the outlier test's own strict comparison).  The
+maximum and the 99th percentile of the K column maxima are summaries for the
+reader (torch reductions over K values), not a step of the matmul path.
 """
 
 from __future__ import annotations
@@ -48,12 +48,18 @@ def outlier_stats(X, thresholds: Iterable[float] = DEFAULT_THRESHOLDS,
     c = cm.float()
     mx = float(c.max())
     q99 = float(torch.quantile(c, 0.99))
-    counts = {}
+    ts = []
     for t in thresholds:
         t = float(t)
         if t != t or t < 0:
             raise ValueError("thresholds must be non-negative numbers")
-        counts[t] = int((c > t).sum())
+        ts.append(t)
+    counts = {}
+    lim = binding.INT8MM_MAX_COUNT_THRESHOLDS
+    for i in range(0, len(ts), lim):
+        part = ts[i:i + lim]
+        got = binding.int8_outlier_counts(cm, part).cpu().tolist()
+        counts.update({t: int(n) for t, n in zip(part, got)})
     out.update(max=mx, q99=q99, ratio=(mx / q99) if q99 > 0 else float("inf"),
                n_outliers=counts, fp16_fraction={t: n / K for t, n in counts.items()})
     return out

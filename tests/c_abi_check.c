@@ -25,6 +25,10 @@ int main(void) {
   printf("profiled %d\n", int8_matmul_profiled(FAKE, 4, 8, FAKE, FAKE, 4, -1.0f, FAKE, FAKE_WS,
                                                1u << 30, NULL, NULL, NULL));
   printf("colmax %d\n", int8_column_absmax(FAKE, 4, 8, NULL, FAKE_WS, 1u << 30, NULL));
+  {
+    const float thr[2] = {6.0f, NAN};
+    printf("counts %d\n", int8_outlier_counts(FAKE, 8, thr, 2, FAKE, NULL));
+  }
   printf("empty %d\n", int8_matmul(NULL, 0, 8, NULL, FAKE, 4, 6.0f, NULL, NULL, 0, NULL));
   printf("strerror %s\n", int8mm_strerror(INT8MM_EWORKSPACE));
   printf("hiperr [%s]\n", int8mm_last_hip_error());

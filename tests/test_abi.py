@@ -43,7 +43,7 @@ def test_header_declares_the_boundary():
                           "int8_matmul", "int8_linear", "int8_matmul_stages", "int8_matmul_profiled",
                           "int8_column_absmax", "int8mm_strerror", "int8mm_last_hip_error",
                           "int8_matmul_noalloc", "int8_matmul_noalloc_max_workspace",
-                          "int8_pack_weight"])
+                          "int8_pack_weight", "int8_outlier_counts"])
     assert set(fns) == set(binding.SIGNATURES)
 
 
@@ -74,6 +74,7 @@ def test_header_constants_match_binding():
     assert int(consts["INT8MM_ESCRATCH"]) == binding.INT8MM_ESCRATCH
     assert int(consts["INT8MM_MAX_K"]) == binding.INT8MM_MAX_K
     assert int(consts["INT8MM_DECODE_MAX_M"]) == binding.INT8MM_DECODE_MAX_M
+    assert int(consts["INT8MM_MAX_COUNT_THRESHOLDS"]) == binding.INT8MM_MAX_COUNT_THRESHOLDS
 
 
 def test_int32_accumulator_bound():
@@ -201,6 +202,28 @@ def test_column_absmax_rejects_bad_arguments(lib):
     need = lib.int8_matmul_workspace_size(40, 8, 0)
     assert f(FAKE, 40, 8, FAKE, FAKE_WS, need - 1, None) == binding.INT8MM_EWORKSPACE
     assert f(None, 4, 0, None, None, 0, None) == binding.INT8MM_OK  # K == 0: nothing to do
+
+
+def _thr(*ts):
+    return (ctypes.c_float * max(len(ts), 1))(*ts)
+
+
+def test_outlier_counts_rejects_bad_arguments(lib):
+    f = lib.int8_outlier_counts
+    ok = _thr(0.0, 6.0, math.inf)
+    assert f(FAKE, -1, ok, 3, FAKE, None) == binding.INT8MM_ESHAPE
+    assert f(FAKE, binding.INT8MM_MAX_K + 1, ok, 3, FAKE, None) == binding.INT8MM_ESHAPE
+    assert f(None, 8, ok, 3, FAKE, None) == binding.INT8MM_EINVAL        # no colmax
+    assert f(FAKE, 8, None, 3, FAKE, None) == binding.INT8MM_EINVAL      # no thresholds
+    assert f(FAKE, 8, ok, 3, None, None) == binding.INT8MM_EINVAL        # no counts
+    assert f(FAKE, 8, ok, 0, FAKE, None) == binding.INT8MM_EINVAL        # none asked for
+    lim = binding.INT8MM_MAX_COUNT_THRESHOLDS
+    many = _thr(*([6.0] * (lim + 1)))
+    assert f(FAKE, 8, many, lim + 1, FAKE, None) == binding.INT8MM_EINVAL
+    assert f(FAKE, 8, _thr(6.0, math.nan), 2, FAKE, None) == binding.INT8MM_EINVAL
+    assert f(FAKE, 8, _thr(-1.0), 1, FAKE, None) == binding.INT8MM_EINVAL
+    assert f(FAKE + 1, 8, ok, 3, FAKE, None) == binding.INT8MM_EINVAL    # misaligned colmax
+    assert f(FAKE, 8, ok, 3, FAKE + 2, None) == binding.INT8MM_EINVAL    # misaligned counts
 
 
 def test_stages_rejects_bad_arguments(lib):

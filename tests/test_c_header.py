@@ -46,6 +46,7 @@ def test_c_client_gets_documented_statuses(c_program):
     assert int(got["stages"]) == binding.INT8MM_EWORKSPACE  # no workspace
     assert int(got["profiled"]) == binding.INT8MM_EINVAL    # negative threshold
     assert int(got["colmax"]) == binding.INT8MM_EINVAL      # no output
+    assert int(got["counts"]) == binding.INT8MM_EINVAL      # NaN threshold
     assert int(got["empty"]) == binding.INT8MM_OK           # M == 0
     assert got["strerror"].startswith("workspace")
     assert got["hiperr"] == "[]"

@@ -34,13 +34,56 @@ def test_column_absmax_parity(lib, M, K, n_out):
     assert not (got.view(np.uint16) & 0x8000).any()  # maxima of |x|: no negative zero
 
 
+@pytest.mark.parametrize("M,K", [(512, 2048), (7, 37), (3, 1), (64, 5000)])
+def test_outlier_counts_parity(lib, M, K):
+    """int8_outlier_counts against the oracle's |O| at each threshold,
+    including thresholds equal to a column maximum (strict: not counted)."""
+    print(f"case outlier_counts M={M} K={K}", flush=True)
+    import torch
+    X, _ = workloads.make_x(M, K, 3 * M + K, min(3, K), 8.0, 60.0, "uniform")
+    rng = np.random.default_rng(K)
+    cols = rng.choice(K, min(K, 9), replace=False)
+    X[:, cols] = (rng.standard_t(3, size=(M, cols.size)) * 2).astype(np.float16)
+    _, _, colmax = ref.outlier_mask_ref(X, 6.0)
+    ties = [float(v) for v in np.unique(colmax)[-5:]]  # exact column maxima
+    ts = [0.0, 0.5, 2.0, 5.0, 6.0, 7.0, 60.0, math.inf] + ties
+    cm = lib.int8_column_absmax(to_dev(X))
+    got = lib.int8_outlier_counts(cm, ts)
+    torch.cuda.synchronize()
+    assert got.dtype == torch.int32 and got.shape == (len(ts),)
+    for t, n in zip(ts, got.cpu().tolist()):
+        _, O, _ = ref.outlier_mask_ref(X, t)
+        assert n == O.size, t
+
+
+def test_outlier_counts_edge_cases(lib):
+    import torch
+    # K == 0: every count is zero
+    empty = torch.empty((0,), dtype=torch.float16, device="cuda")
+    z = lib.int8_outlier_counts(empty, [0.0, 6.0])
+    # every threshold slot at the limit; an infinite column maximum counts
+    # only below +inf
+    cm = torch.tensor([0.0, 6.0, 6.00390625, float("inf"), 1.0], dtype=torch.float16,
+                      device="cuda")
+    lim = lib.binding.INT8MM_MAX_COUNT_THRESHOLDS
+    ts = [0.0, 6.0, 1e30, math.inf] + [float(i) / 8 for i in range(lim - 4)]
+    got = lib.int8_outlier_counts(cm, ts)
+    torch.cuda.synchronize()
+    assert z.cpu().tolist() == [0, 0]
+    vals = [0.0, 6.0, 6.00390625, math.inf, 1.0]
+    assert got.cpu().tolist() == [sum(v > t for v in vals) for t in ts]
+    with pytest.raises(lib.Int8mmError):
+        lib.int8_outlier_counts(cm, [6.0] * (lim + 1))
+
+
 def test_outlier_stats_counts_match_oracle(lib):
     import torch
     X, _ = workloads.make_x(512, 2048, 77, 0, 8.0, 60.0, "uniform")
     rng = np.random.default_rng(5)
     cols = rng.choice(2048, 21, replace=False)
     X[:, cols] = (rng.standard_t(3, size=(512, 21)) * 2).astype(np.float16)  # heavy tails
-    ts = (0.0, 1.0, 3.0, 5.0, 6.0, 7.0, 12.0, math.inf)
+    # more thresholds than one int8_outlier_counts call takes
+    ts = (0.0, 1.0, 3.0, 5.0, 6.0, 7.0, 12.0, math.inf) + tuple(0.25 * i + 0.1 for i in range(70))
     st = lib.outlier_stats(to_dev(X), thresholds=ts)
     torch.cuda.synchronize()
     for t in ts:

@@ -88,6 +88,13 @@ SHAPES = [
     # first half of each pair computes the whole tile)
     (2200, 96, 7600, 3, 6.0),
     (2200, 256, 7600, 100, 6.0),
+    # more rows than one pass of the row-pass blocks covers: a wave per row
+    # beyond 4 * 2048 rows (two and three passes), a block per row beyond
+    # 2048 rows, and the streamed form (unaligned rows) beyond 8192 rows
+    (8300, 256, 72, 3, 6.0),
+    (20000, 128, 40, 2, 6.0),
+    (2100, 9000, 64, 5, 6.0),
+    (8250, 100, 40, 2, 6.0),
 ]
 
 

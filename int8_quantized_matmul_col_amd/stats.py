@@ -34,7 +34,11 @@ def outlier_stats(X, thresholds: Iterable[float] = DEFAULT_THRESHOLDS,
       column maxima; ``ratio`` = max / q99 (about 1 without outlier columns);
     * ``n_outliers[t]`` -- |O| at threshold t (columns with colmax > t);
     * ``fp16_fraction[t]`` -- |O| / K, the share of the multiply-adds that
-      take the fp16 path at t.
+      take the fp16 path at t;
+    * ``histogram`` -- the column maxima binned at the thresholds, from the
+      same counts: a list of (lo, hi, n), n = columns with lo < colmax <= hi,
+      the first bin from lo = -inf (colmax <= the smallest threshold), the
+      last up to hi = +inf (above the largest finite threshold).
 
     ``colmax`` may be passed if it was already computed.
     """
@@ -43,7 +47,8 @@ def outlier_stats(X, thresholds: Iterable[float] = DEFAULT_THRESHOLDS,
     M, K = X.shape
     out: Dict[str, object] = {"M": int(M), "K": int(K)}
     if K == 0:
-        out.update(max=0.0, q99=0.0, ratio=float("nan"), n_outliers={}, fp16_fraction={})
+        out.update(max=0.0, q99=0.0, ratio=float("nan"), n_outliers={}, fp16_fraction={},
+                   histogram=[])
         return out
     c = cm.float()
     mx = float(c.max())
@@ -60,8 +65,19 @@ def outlier_stats(X, thresholds: Iterable[float] = DEFAULT_THRESHOLDS,
         part = ts[i:i + lim]
         got = binding.int8_outlier_counts(cm, part).cpu().tolist()
         counts.update({t: int(n) for t, n in zip(part, got)})
+    edges = sorted(counts)
+    if not edges:
+        edges = [float("inf")]
+        counts_inf = {float("inf"): 0}
+    else:
+        counts_inf = counts
+    hist = [(float("-inf"), edges[0], K - counts_inf[edges[0]])]
+    hist += [(lo, hi, counts_inf[lo] - counts_inf[hi]) for lo, hi in zip(edges, edges[1:])]
+    if edges[-1] != float("inf"):
+        hist.append((edges[-1], float("inf"), counts_inf[edges[-1]]))
     out.update(max=mx, q99=q99, ratio=(mx / q99) if q99 > 0 else float("inf"),
-               n_outliers=counts, fp16_fraction={t: n / K for t, n in counts.items()})
+               n_outliers=counts, fp16_fraction={t: n / K for t, n in counts.items()},
+               histogram=hist)
     return out
 
 

@@ -92,6 +92,13 @@ def test_outlier_stats_counts_match_oracle(lib):
         assert st["fp16_fraction"][t] == O.size / 2048
     _, _, colmax = ref.outlier_mask_ref(X, 6.0)
     assert st["max"] == float(colmax.max())
+    # the histogram bins the oracle's column maxima at the sorted thresholds
+    hist = st["histogram"]
+    assert sum(n for _, _, n in hist) == 2048
+    edges = sorted(set(ts))
+    assert [h[1] for h in hist] == edges and hist[0][0] == -math.inf
+    for lo, hi, n in hist:
+        assert n == int(np.sum((colmax > lo) & (colmax <= hi))), (lo, hi)
     # the percentile interpolates between two column maxima in fp32 on the GPU
     assert st["q99"] == pytest.approx(float(np.quantile(colmax.astype(np.float64), 0.99)), rel=1e-4)
     assert st["ratio"] > 1.5  # heavy-tailed columns stand out

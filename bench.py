@@ -543,10 +543,30 @@ def measure_ceilings(torch, dev) -> dict:
     if st != 0:
         raise SystemExit(f"read probe failed: HIP error {st}")
     res["hbm_read_GB/s"] = round(v.value / 1e9, 1)
+    del buf
+    # the same stream over four rotating copies of 224 MiB (the decode
+    # weight's size), one per launch, back to back: the rate a decode-sized
+    # read reaches with its launch ramp and tail
+    pl.int8mm_probe_read_copies.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.POINTER(ctypes.c_double)]
+    cb, copies = 224 << 20, 4
+    buf = torch.ones(cb * copies // 4, dtype=torch.int32, device=dev)
+    best = 0.0
+    for nb in (256, 512):
+        v = ctypes.c_double()
+        st = pl.int8mm_probe_read_copies(ctypes.c_void_p(buf.data_ptr()), cb, copies, nb,
+                                         ctypes.c_void_p(rout.data_ptr()), ctypes.byref(v))
+        if st != 0:
+            raise SystemExit(f"read probe failed: HIP error {st}")
+        best = max(best, v.value)
+    res["hbm_read_224MiB_GB/s"] = round(best / 1e9, 1)
     res["method"] = ("int8mm_probe_mfma_i8: 4 waves per SIMD, 16 independent "
                      "v_mfma_i32_32x32x32_i8 accumulators each, 2000 iterations; "
                      "int8mm_probe_read: 2048 workgroups, each a contiguous chunk of 2 GiB, "
-                     "8 x 16-byte loads per lane in flight (libint8mm_ceilings.so)")
+                     "8 x 16-byte loads per lane in flight; int8mm_probe_read_copies: the same "
+                     "kernel over 4 rotating 224 MiB copies (the decode weight's size), one per "
+                     "launch, 256 or 512 workgroups, the better (libint8mm_ceilings.so)")
     del buf
     torch.cuda.empty_cache()
     return res
@@ -631,9 +651,12 @@ def main() -> int:
     if not args.no_ceilings:
         log("[bench] measuring the MFMA and HBM ceilings ...")
         ceilings = measure_ceilings(torch, dev)
-        head["roofline"]["frac_of_measured_ceiling"] = frac_of_ceiling(head["roofline"], ceilings)
-        for r in extra.values():
-            r["roofline"]["frac_of_measured_ceiling"] = frac_of_ceiling(r["roofline"], ceilings)
+        for roof in [head["roofline"]] + [r["roofline"] for r in extra.values()]:
+            roof["frac_of_measured_ceiling"] = frac_of_ceiling(roof, ceilings)
+            if roof["unit"] == "GB/s":
+                # against a stream of the decode weight's size (ramp and tail included)
+                roof["frac_of_224MiB_read"] = round(
+                    roof["achieved"] / ceilings["hbm_read_224MiB_GB/s"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -143,4 +143,32 @@ __attribute__((visibility("default"))) int int8mm_probe_read(const void* src, si
   return 0;
 }
 
+// The same stream over `copies` buffers of `bytes` each (src, src + bytes,
+// ...), launch r reading copy r % copies: with copies * bytes beyond the
+// 256 MB MALL every launch reads from HBM, and a buffer the size of one call's
+// operand gives the rate of back-to-back launches of that size (ramp and
+// tail included).  bytes must be a multiple of blocks * 256 * 8 * 16.
+__attribute__((visibility("default"))) int int8mm_probe_read_copies(const void* src,
+                                                                    size_t bytes, int copies,
+                                                                    int blocks, int* out,
+                                                                    double* bytes_per_s) {
+  const size_t unit = (size_t)blocks * 256 * kReadU * 16;
+  if (src == nullptr || out == nullptr || bytes_per_s == nullptr || blocks <= 0 ||
+      copies <= 0 || bytes == 0 || bytes % unit != 0)
+    return (int)hipErrorInvalidValue;
+  const size_t per = bytes / 16 / (size_t)blocks;
+  float ms = 0.0f;
+  const int reps = 5 * copies;
+  int r = 0;
+  hipError_t e = timed(
+      [&] {
+        const v4i* c = static_cast<const v4i*>(src) + (size_t)(r++ % copies) * (bytes / 16);
+        hipLaunchKernelGGL(k_read_chunk, dim3(blocks), dim3(256), 0, nullptr, c, per, out);
+      },
+      reps, &ms);
+  if (e != hipSuccess) return (int)e;
+  *bytes_per_s = (double)reps * bytes / (ms * 1e-3);
+  return 0;
+}
+
 }  // extern "C"

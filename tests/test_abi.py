@@ -58,7 +58,7 @@ def test_probe_library_loads_and_exports_the_probes(lib):
     from int8_quantized_matmul_col_amd import build
     assert os.path.exists(build.PROBE_LIB_PATH)
     probes = ctypes.CDLL(build.PROBE_LIB_PATH)
-    for name in ("int8mm_probe_mfma_i8", "int8mm_probe_read"):
+    for name in ("int8mm_probe_mfma_i8", "int8mm_probe_read", "int8mm_probe_read_copies"):
         assert hasattr(probes, name), name
     assert not hasattr(lib, "int8mm_probe_read")
 

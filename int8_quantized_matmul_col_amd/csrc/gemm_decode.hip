@@ -35,6 +35,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kU = 2;  // K steps per loop iteration
 constexpr int kSlots = 8;  // outlier K steps parked in LDS (more: static schedule)
+constexpr int kSparseCols = 4;  // single row: outlier columns per step taken one by one
 constexpr int kMaxWords = (133144 + 63) / 64 * 2;  // mask words for the largest K
 // single-row calls code X in the kernel up to this padded row length (its
 // codes are held in LDS beside the reduction and outlier-slot buffers)
@@ -65,6 +66,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   __shared__ int s_slot_step[kSlots];
   __shared__ int s_nslots;
   __shared__ int s_next;
+  __shared__ float s_aw[G * 16];    // w_scale of the workgroup's rows
+  __shared__ float s_bias[G * 16];  // their biases (0 without)
+  __shared__ float s_ax[16];        // x_scale of the rows (activation pass)
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nw = ldk / 32;
@@ -122,12 +126,23 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     load_w(first, b);
     if constexpr (!ROW) load_x(first, a);
   }
+  // the scales and biases the fp16 outlier pass and the epilogue need, also
+  // requested now (one value per thread; into LDS at the set-up's barrier)
+  const int sn = min(n_base + t, N - 1);
+  const float pre_aw = t < G * 16 ? w_scale[sn] : 0.0f;
+  const float pre_b = t < G * 16 && bias != nullptr ? h2f(bias[sn]) : 0.0f;
+  const float pre_ax = !ROW && t < 16 && t < M ? x_scale[t] : 0.0f;
 
   if (t == 0) {
     s_nslots = 0;
     s_next = kEarly ? kWaves * kU : 0;  // the dynamic schedule hands out the steps after the first chunks
   }
   float ax = 0.0f;  // ROW: a_x of the row
+  // ROW: the row's 8-column chunks that hold outlier columns, kept in the
+  // reduction buffer (unused until the end) for the fp16 pass; needs
+  // kRowMaxLdk*2 bytes there (G >= 4)
+  constexpr bool kRowStash = ROW && G * 256 * kWaves * 4 >= kRowMaxLdk * 2;
+  uint4* s_xrow = reinterpret_cast<uint4*>(&s_red[0][0]);
   if constexpr (ROW) {
     // mask bytes (strict |x| > threshold; padding columns k >= K never), the
     // absmax over the regular columns, then the codes of the row into LDS
@@ -172,11 +187,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
         q.x &= keep_bytes(ob[u] & 0xfu);
         q.y &= keep_bytes(ob[u] >> 4);
         s_xq2[c] = q;
+        // the X values of the chunk's outlier columns, for the fp16 pass
+        if (kRowStash && ob[u] != 0u) s_xrow[c] = hv[u];
       }
     }
   } else {
     for (int w = t; w < nw; w += kThreads) s_bits[w] = mask_bits[w];
   }
+  if (t < G * 16) {
+    s_aw[t] = pre_aw;
+    s_bias[t] = pre_b;
+  }
+  if (!ROW && t < 16) s_ax[t] = pre_ax;
   __syncthreads();
   // K steps holding outlier columns, in ascending order (one wave, ballots)
   if (wave == 0) {
@@ -215,16 +237,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     const int k0 = s * 64 + kq;
     const uint32_t obits = (s_bits[k0 >> 5] >> (k0 & 31)) & 0xffffu;
     v8h xa[2];
+    if constexpr (kRowStash) {
+      // the two stashed chunks of columns k0 .. k0+15 (only their outlier
+      // entries were written and only those are used)
+      const uint4 c0 = s_xrow[k0 >> 3], c1 = s_xrow[(k0 >> 3) + 1];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      uint16_t v = 0;
-      if (((obits >> e) & 1u) && xvalid) v = X[(size_t)ml * K + k0 + e];
-      xa[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
+      for (int e = 0; e < 16; ++e) {
+        uint16_t v = 0;
+        if (((obits >> e) & 1u) && xvalid) v = (uint16_t)half_at(e < 8 ? c0 : c1, e & 7);
+        xa[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        uint16_t v = 0;
+        if (((obits >> e) & 1u) && xvalid) v = X[(size_t)ml * K + k0 + e];
+        xa[e >> 3][e & 7] = __builtin_bit_cast(_Float16, v);
+      }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int n = min(n_base + g * 16 + ml, N - 1);
-      const float aw = w_scale[n];
+      const float aw = s_aw[g * 16 + ml];
       v8h wb[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -296,10 +329,40 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     __syncthreads();
     // fp16 outlier term, slot k on wave k % kWaves, in slot order
     for (int k = wave; k < n_oslots; k += kWaves) {
+      const int st = s_slot_step[k];
+      if constexpr (kRowStash) {
+        // the single row, a step with few outlier columns: each column's
+        // product x * W_O[n] added with an fma straight into the lanes that
+        // hold row 0 of the accumulator (lanes 0..15, element 0, column n =
+        // n_base + 16 g + lane), the int8 code read from the parked
+        // fragment of the lane that loaded it (byte c % 16 of lane
+        // lane + 16 (c / 16)); the same single rounding per product as the
+        // MFMA form, without building 16-column fragments that are almost
+        // all zero
+        uint64_t cols = ((uint64_t)s_bits[2 * st + 1] << 32) | s_bits[2 * st];
+        if (__popcll(cols) <= kSparseCols) {
+          const uint32_t* slot32 = reinterpret_cast<const uint32_t*>(&s_wslot[k][0][0]);
+          while (cols != 0ull) {
+            const int c = __builtin_ctzll(cols);  // column within the step (wave-uniform)
+            cols &= cols - 1ull;
+            const int col = st * 64 + c;
+            const float x = h2f((uint16_t)half_at(s_xrow[col >> 3], col & 7));
+            const int src = (lane & 15) + 16 * (c >> 4);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const uint32_t word = slot32[(g * 64 + src) * 4 + ((c & 15) >> 2)];
+              const int q = (int)(int8_t)((word >> ((c & 3) * 8)) & 0xffu);
+              const float wo = h2f(dequant_w_half(q, s_aw[g * 16 + (lane & 15)]));
+              if (lane < 16) acco[g][0] = fmaf(x, wo, acco[g][0]);
+            }
+          }
+          continue;
+        }
+      }
       v4i bw[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) bw[g] = s_wslot[k][g][lane];
-      outlier_step(s_slot_step[k], bw);
+      outlier_step(st, bw);
     }
   } else {
     // the steps after the first chunks split evenly over the waves, kU per
@@ -337,6 +400,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
       outlier_step(st, bw);
     }
   }
+
+  // the stashed row lives in the reduction buffer: every wave is done with it
+  if constexpr (kRowStash) __syncthreads();
 
   // ---- fixed-order reduction of the 8 wave partials.  Element e = g*256 +
   // lane*4 + r of a wave holds result row m = 4*(lane/16) + r, column
@@ -390,8 +456,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     if (MODE == 1) {
       C[(size_t)m * N + n] = csum[u];
     } else {
-      const float sc = (ROW ? ax : x_scale[m]) * w_scale[n] * kInv127Sq;
-      const float b = bias != nullptr ? h2f(bias[n]) : 0.0f;
+      const float sc = (ROW ? ax : s_ax[m]) * s_aw[g * 16 + (ln & 15)] * kInv127Sq;
+      const float b = s_bias[g * 16 + (ln & 15)];
       Y[(size_t)m * N + n] = f2h((float)csum[u] * sc + osum[u] + b);
     }
   }

@@ -35,7 +35,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kU = 2;  // K steps per loop iteration
 constexpr int kSlots = 8;  // outlier K steps parked in LDS (more: static schedule)
-constexpr int kSparseCols = 4;  // single row: outlier columns per step taken one by one
+constexpr int kSparseCols = 4;  // outlier columns per step taken one by one (fma form)
 constexpr int kMaxWords = (133144 + 63) / 64 * 2;  // mask words for the largest K
 // single-row calls code X in the kernel up to this padded row length (its
 // codes are held in LDS beside the reduction and outlier-slot buffers)
@@ -330,15 +330,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     // fp16 outlier term, slot k on wave k % kWaves, in slot order
     for (int k = wave; k < n_oslots; k += kWaves) {
       const int st = s_slot_step[k];
-      if constexpr (kRowStash) {
-        // the single row, a step with few outlier columns: each column's
-        // product x * W_O[n] added with an fma straight into the lanes that
-        // hold row 0 of the accumulator (lanes 0..15, element 0, column n =
-        // n_base + 16 g + lane), the int8 code read from the parked
-        // fragment of the lane that loaded it (byte c % 16 of lane
-        // lane + 16 (c / 16)); the same single rounding per product as the
-        // MFMA form, without building 16-column fragments that are almost
-        // all zero
+      // A step with few outlier columns: each column's products x[m] *
+      // W_O[n] added with fmas straight into the accumulator (lane l holds
+      // rows m = 4 (l / 16) + r, r < 4, of column n = n_base + 16 g + l % 16),
+      // the int8 code read from the parked fragment of the lane that loaded
+      // it (byte c % 16 of lane l % 16 + 16 (c / 16)) -- the same single
+      // rounding per product as the MFMA form, without building 16-column
+      // fragments that are almost all zero.  X values: the stashed row (one
+      // row), else X itself.
+      if (!ROW || kRowStash) {
         uint64_t cols = ((uint64_t)s_bits[2 * st + 1] << 32) | s_bits[2 * st];
         if (__popcll(cols) <= kSparseCols) {
           const uint32_t* slot32 = reinterpret_cast<const uint32_t*>(&s_wslot[k][0][0]);
@@ -346,14 +346,32 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
             const int c = __builtin_ctzll(cols);  // column within the step (wave-uniform)
             cols &= cols - 1ull;
             const int col = st * 64 + c;
-            const float x = h2f((uint16_t)half_at(s_xrow[col >> 3], col & 7));
             const int src = (lane & 15) + 16 * (c >> 4);
+            if constexpr (ROW) {
+              // the single row is row 0 of the accumulator: lanes 0..15, element 0
+              const float x = h2f((uint16_t)half_at(s_xrow[col >> 3], col & 7));
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-              const uint32_t word = slot32[(g * 64 + src) * 4 + ((c & 15) >> 2)];
-              const int q = (int)(int8_t)((word >> ((c & 3) * 8)) & 0xffu);
-              const float wo = h2f(dequant_w_half(q, s_aw[g * 16 + (lane & 15)]));
-              if (lane < 16) acco[g][0] = fmaf(x, wo, acco[g][0]);
+              for (int g = 0; g < G; ++g) {
+                const uint32_t word = slot32[(g * 64 + src) * 4 + ((c & 15) >> 2)];
+                const int q = (int)(int8_t)((word >> ((c & 3) * 8)) & 0xffu);
+                const float wo = h2f(dequant_w_half(q, s_aw[g * 16 + (lane & 15)]));
+                if (lane < 16) acco[g][0] = fmaf(x, wo, acco[g][0]);
+              }
+            } else {
+              float xr[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int m = 4 * (lane >> 4) + r;
+                xr[r] = m < M ? h2f(X[(size_t)m * K + col]) : 0.0f;
+              }
+#pragma unroll
+              for (int g = 0; g < G; ++g) {
+                const uint32_t word = slot32[(g * 64 + src) * 4 + ((c & 15) >> 2)];
+                const int q = (int)(int8_t)((word >> ((c & 3) * 8)) & 0xffu);
+                const float wo = h2f(dequant_w_half(q, s_aw[g * 16 + (lane & 15)]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acco[g][r] = fmaf(xr[r], wo, acco[g][r]);
+              }
             }
           }
           continue;

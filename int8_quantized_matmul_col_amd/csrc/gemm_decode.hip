@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   __shared__ int s_nslots;
   __shared__ int s_next;
   __shared__ float s_aw[G * 16];    // w_scale of the workgroup's rows
-  __shared__ float s_bias[G * 16];  // their biases (0 without)
+  __shared__ uint32_t s_bias[G * 16];  // their biases' binary16 bits (0 without)
   __shared__ float s_ax[16];        // x_scale of the rows (activation pass)
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -120,18 +120,35 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   // registers: there every step goes through the schedules below.)
   constexpr bool kEarly = G <= 7;
   const int first = kEarly ? wave * kU : ldk;
+  // The set-up's own loads go first: loads complete in issue order, so
+  // requested after the first weight chunk they would hold the set-up until
+  // the whole chunk had arrived (and the next chunk is requested only after
+  // the set-up).  The scales and biases the fp16 outlier pass and the
+  // epilogue need (one value per thread, into LDS at the set-up's barrier),
+  // the first mask words (activation pass) or the row of X (single row).
+  const int sn = min(n_base + t, N - 1);
+  const float pre_aw = t < G * 16 ? w_scale[sn] : 0.0f;
+  // (the bias as its bits, converted where it is used: a conversion here
+  // would wait for the load at once)
+  const uint16_t pre_b = t < G * 16 && bias != nullptr ? bias[sn] : (uint16_t)0;
+  const float pre_ax = !ROW && t < 16 && t < M ? x_scale[t] : 0.0f;
+  const uint32_t pre_mw = !ROW && t < nw ? mask_bits[t] : 0u;
+  const int nck = K >> 3;  // ROW: whole 8-column chunks of the row
+  uint4 hv[ROW ? kRowChunks : 1];
+  if constexpr (ROW) {
+    const uint4* xr = reinterpret_cast<const uint4*>(X);
+#pragma unroll
+    for (int u = 0; u < kRowChunks; ++u) {
+      const int c = t + u * kThreads;
+      hv[u] = c < nck ? xr[c] : uint4{0u, 0u, 0u, 0u};
+    }
+  }
   v4i b[kU][G];
   v4i a[kU];
   if constexpr (kEarly) {
     load_w(first, b);
     if constexpr (!ROW) load_x(first, a);
   }
-  // the scales and biases the fp16 outlier pass and the epilogue need, also
-  // requested now (one value per thread; into LDS at the set-up's barrier)
-  const int sn = min(n_base + t, N - 1);
-  const float pre_aw = t < G * 16 ? w_scale[sn] : 0.0f;
-  const float pre_b = t < G * 16 && bias != nullptr ? h2f(bias[sn]) : 0.0f;
-  const float pre_ax = !ROW && t < 16 && t < M ? x_scale[t] : 0.0f;
 
   if (t == 0) {
     s_nslots = 0;
@@ -146,16 +163,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   if constexpr (ROW) {
     // mask bytes (strict |x| > threshold; padding columns k >= K never), the
     // absmax over the regular columns, then the codes of the row into LDS
-    const int nch = ldk / 8, nck = K >> 3;
+    const int nch = ldk / 8;
     uint8_t* s_ob = reinterpret_cast<uint8_t*>(s_bits);  // mask byte of chunk c
-    const uint4* xr = reinterpret_cast<const uint4*>(X);
-    uint4 hv[kRowChunks];
     uint32_t ob[kRowChunks];
-#pragma unroll
-    for (int u = 0; u < kRowChunks; ++u) {
-      const int c = t + u * kThreads;
-      hv[u] = c < nck ? xr[c] : uint4{0u, 0u, 0u, 0u};
-    }
     uint32_t mx2 = 0;
 #pragma unroll
     for (int u = 0; u < kRowChunks; ++u) {
@@ -192,7 +202,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
       }
     }
   } else {
-    for (int w = t; w < nw; w += kThreads) s_bits[w] = mask_bits[w];
+    if (t < nw) s_bits[t] = pre_mw;
+    for (int w = t + kThreads; w < nw; w += kThreads) s_bits[w] = mask_bits[w];
   }
   if (t < G * 16) {
     s_aw[t] = pre_aw;
@@ -475,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
       C[(size_t)m * N + n] = csum[u];
     } else {
       const float sc = (ROW ? ax : s_ax[m]) * s_aw[g * 16 + (ln & 15)] * kInv127Sq;
-      const float b = s_bias[g * 16 + (ln & 15)];
+      const float b = h2f((uint16_t)s_bias[g * 16 + (ln & 15)]);
       Y[(size_t)m * N + n] = f2h((float)csum[u] * sc + osum[u] + b);
     }
   }

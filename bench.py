@@ -481,7 +481,9 @@ def measure(mm, lib, ev, dev, case, t, steps, warmup, rotate=None, others=False,
         peak = PEAK_FP16_TOPS if n_out == K else PEAK_INT8_TOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "algorithmic_ops_per_launch": ops}
-    roof["traffic"] = committed_traffic(case.name, src_hash)
+    # the committed counters were taken at the workload's own threshold (another
+    # threshold changes |O| and, past three fp16 steps, the kernel's branch)
+    roof["traffic"] = committed_traffic(case.name, src_hash) if t == case.threshold else None
     roof["kernel"] = "k_gemm_decode" if decode else "k_gemm_prefill"
     roof["kernel_ms"] = round(kern_avg, 5)
     roof["kernel_timing"] = (f"HIP events stamped by the {roof['kernel']} dispatch, mean of {steps} "

@@ -143,11 +143,11 @@ int run(const uint16_t* X, int64_t M, int64_t K, const int8_t* Wq, const float* 
     return INT8MM_OK;
   }
 
-  // One row with only Y asked for: a single launch that codes X itself.
+  // Up to four rows with only Y asked for: a single launch that codes X itself.
   const bool stage_out = out.mask || out.n_outliers || out.outlier_idx || out.Xq ||
                          out.x_scale || out.X_O || out.W_O || out.C;
-  if (L.decode && !stage_out && out.Y != nullptr && i8mm::gemm_decode_row_ok(X, m, k, ldk)) {
-    if ((e = i8mm::launch_gemm_decode_row(X, k, ldk, threshold, Wq, n, w_scale, bias, out.Y, s,
+  if (L.decode && !stage_out && out.Y != nullptr && i8mm::gemm_decode_row_ok(X, m, k, ldk, n)) {
+    if ((e = i8mm::launch_gemm_decode_row(X, m, k, ldk, threshold, Wq, n, w_scale, bias, out.Y, s,
                                           ev_start, ev_stop)) != hipSuccess)
       return hip_fail(e);
     return INT8MM_OK;

@@ -40,7 +40,13 @@ constexpr int kMaxWords = (133144 + 63) / 64 * 2;  // mask words for the largest
 // single-row calls code X in the kernel up to this padded row length (its
 // codes are held in LDS beside the reduction and outlier-slot buffers)
 constexpr int kRowMaxLdk = 16384;
-constexpr int kRowChunks = kRowMaxLdk / 8 / kThreads;  // 8-column chunks per thread
+// two to four rows coded here: up to this padded row length
+constexpr int kRowsMaxLdk = 8192;
+// ... and up to this many groups of 16 weight rows per workgroup (LDS)
+constexpr int kRowsMaxG = 7;
+// padded row length and 8-column chunks per thread and row, by RR
+constexpr int row_max_ldk(int rr) { return rr == 1 ? kRowMaxLdk : kRowsMaxLdk; }
+constexpr int row_chunks(int rr) { return rr == 0 ? 1 : row_max_ldk(rr) / 8 / kThreads; }
 }  // namespace
 
 // A 16-byte Wq fragment.  The weight is read once per call and never again
@@ -50,19 +56,24 @@ __device__ __forceinline__ v4i wload(const int8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
 }
 
-// ROW: M == 1 and X coded here (Xq, x_scale and mask_bits unused); else the
-// codes, scales and mask words come from the activation pass.
-template <int G, int MODE, bool ROW>  // MODE 0: Y, 1: int32 C
+// RR > 0: the M <= RR rows of X coded here (Xq, x_scale and mask_bits
+// unused; RR = 1 for one row, RR = 4 for two to four rows, which repeat row
+// M-1 up to four); RR = 0: the codes, scales and mask words come from the
+// activation pass.
+template <int G, int MODE, int RR>  // MODE 0: Y, 1: int32 C
 __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq, int M, int N, int K, int ldk,
     const float* __restrict__ x_scale, const float* __restrict__ w_scale,
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ mask_bits, float threshold,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C) {
+  constexpr bool ROW = RR > 0;
+  constexpr int kRC = row_chunks(RR);                     // chunks per thread and row
+  constexpr int kXqRow = ROW ? row_max_ldk(RR) / 16 : 1;  // s_xq fragments per row
   __shared__ uint32_t s_bits[ROW ? kRowMaxLdk / 32 : kMaxWords];
   __shared__ int s_red[kWaves][G * 256];
   __shared__ v4i s_wslot[kSlots][G][64];  // Wq fragments of the outlier steps
-  __shared__ v4i s_xq[ROW ? kRowMaxLdk / 16 : 1];  // ROW: the codes of X
-  __shared__ uint32_t s_wmax[kWaves];
+  __shared__ v4i s_xq[ROW ? RR * kXqRow : 1];  // ROW: the codes of X, row by row
+  __shared__ uint32_t s_wmax[ROW ? RR : 1][kWaves];
   __shared__ int s_slot_step[kSlots];
   __shared__ int s_nslots;
   __shared__ int s_next;
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     for (int u = 0; u < kU; ++u) {
       const int st = base + u;
       if constexpr (ROW)
-        a[u] = (ml == 0 && st < nsteps) ? s_xq[(st * 64 + kq) >> 4] : v4i{};
+        a[u] = (ml < M && st < nsteps) ? s_xq[ml * kXqRow + ((st * 64 + kq) >> 4)] : v4i{};
       else
         a[u] = (xvalid && st < nsteps) ? *reinterpret_cast<const v4i*>(xrow + (size_t)st * kTileBytes)
                                        : v4i{};
@@ -134,13 +145,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   const float pre_ax = !ROW && t < 16 && t < M ? x_scale[t] : 0.0f;
   const uint32_t pre_mw = !ROW && t < nw ? mask_bits[t] : 0u;
   const int nck = K >> 3;  // ROW: whole 8-column chunks of the row
-  uint4 hv[ROW ? kRowChunks : 1];
+  uint4 hv[ROW ? RR * kRC : 1];  // row r's chunk t + u*kThreads at hv[r*kRC + u]
   if constexpr (ROW) {
-    const uint4* xr = reinterpret_cast<const uint4*>(X);
 #pragma unroll
-    for (int u = 0; u < kRowChunks; ++u) {
-      const int c = t + u * kThreads;
-      hv[u] = c < nck ? xr[c] : uint4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < RR; ++r) {
+      const uint4* xr = reinterpret_cast<const uint4*>(X + (size_t)min(r, M - 1) * K);
+#pragma unroll
+      for (int u = 0; u < kRC; ++u) {
+        const int c = t + u * kThreads;
+        hv[r * kRC + u] = c < nck ? xr[c] : uint4{0u, 0u, 0u, 0u};
+      }
     }
   }
   v4i b[kU][G];
@@ -158,47 +172,67 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   // ROW: the row's 8-column chunks that hold outlier columns, kept in the
   // reduction buffer (unused until the end) for the fp16 pass; needs
   // kRowMaxLdk*2 bytes there (G >= 4)
-  constexpr bool kRowStash = ROW && G * 256 * kWaves * 4 >= kRowMaxLdk * 2;
+  constexpr bool kRowStash = RR == 1 && G * 256 * kWaves * 4 >= kRowMaxLdk * 2;
   uint4* s_xrow = reinterpret_cast<uint4*>(&s_red[0][0]);
   if constexpr (ROW) {
-    // mask bytes (strict |x| > threshold; padding columns k >= K never), the
-    // absmax over the regular columns, then the codes of the row into LDS
+    // mask bytes (strict colmax > threshold over the rows; padding columns
+    // k >= K never), each row's absmax over the regular columns, then the
+    // codes of the rows into LDS
     const int nch = ldk / 8;
     uint8_t* s_ob = reinterpret_cast<uint8_t*>(s_bits);  // mask byte of chunk c
-    uint32_t ob[kRowChunks];
-    uint32_t mx2 = 0;
+    uint32_t ob[kRC];
 #pragma unroll
-    for (int u = 0; u < kRowChunks; ++u) {
+    for (int u = 0; u < kRC; ++u) {
       const int c = t + u * kThreads;
+      uint32_t m4[4] = {0u, 0u, 0u, 0u};  // |x| bits, two columns per word
+#pragma unroll
+      for (int r = 0; r < RR; ++r) {
+        const uint4 h = hv[r * kRC + u];
+        m4[0] = pk_max_u16(m4[0], h.x & 0x7fff7fffu);
+        m4[1] = pk_max_u16(m4[1], h.y & 0x7fff7fffu);
+        m4[2] = pk_max_u16(m4[2], h.z & 0x7fff7fffu);
+        m4[3] = pk_max_u16(m4[3], h.w & 0x7fff7fffu);
+      }
       uint32_t o = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        o |= (h2f((uint16_t)habs_bits(half_at(hv[u], i))) > threshold ? 1u : 0u) << i;
+        o |= (h2f((uint16_t)((m4[i >> 1] >> ((i & 1) * 16)) & 0xffffu)) > threshold ? 1u : 0u) << i;
       ob[u] = o;
       if (c < nch) s_ob[c] = (uint8_t)o;
-      mx2 = pk_max_u16(mx2, chunk_absmax2(hv[u], o));
     }
-    const uint32_t mw = wave_max(max(mx2 & 0xffffu, mx2 >> 16));
-    if (lane == 0) s_wmax[wave] = mw;
-    __syncthreads();
-    uint32_t mx = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = max(mx, s_wmax[w]);
-    ax = h2f((uint16_t)mx);
-    const float r = ax == 0.0f ? 0.0f : 127.0f / ax;
+    for (int r = 0; r < RR; ++r) {
+      uint32_t mx2 = 0;
+#pragma unroll
+      for (int u = 0; u < kRC; ++u) mx2 = pk_max_u16(mx2, chunk_absmax2(hv[r * kRC + u], ob[u]));
+      const uint32_t mw = wave_max(max(mx2 & 0xffffu, mx2 >> 16));
+      if (lane == 0) s_wmax[r][wave] = mw;
+    }
+    __syncthreads();
     uint2* s_xq2 = reinterpret_cast<uint2*>(s_xq);
 #pragma unroll
-    for (int u = 0; u < kRowChunks; ++u) {
-      const int c = t + u * kThreads;
-      if (c < nch) {
-        float dev;
-        uint2 q = quant8_fast(hv[u], r, &dev);
-        if (dev > kTieGuard) q = quant8_exact(hv[u], ax);
-        q.x &= keep_bytes(ob[u] & 0xfu);
-        q.y &= keep_bytes(ob[u] >> 4);
-        s_xq2[c] = q;
-        // the X values of the chunk's outlier columns, for the fp16 pass
-        if (kRowStash && ob[u] != 0u) s_xrow[c] = hv[u];
+    for (int r = 0; r < RR; ++r) {
+      uint32_t mx = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mx = max(mx, s_wmax[r][w]);
+      const float axr = h2f((uint16_t)mx);
+      if (r == 0) ax = axr;
+      if (RR > 1 && t == r && r < M) s_ax[r] = axr;
+      const float rr = axr == 0.0f ? 0.0f : 127.0f / axr;
+#pragma unroll
+      for (int u = 0; u < kRC; ++u) {
+        const int c = t + u * kThreads;
+        if (r < M && c < nch) {
+          const uint4 h = hv[r * kRC + u];
+          float dev;
+          uint2 q = quant8_fast(h, rr, &dev);
+          if (dev > kTieGuard) q = quant8_exact(h, axr);
+          q.x &= keep_bytes(ob[u] & 0xfu);
+          q.y &= keep_bytes(ob[u] >> 4);
+          s_xq2[r * (kXqRow * 2) + c] = q;
+          // the X values of the chunk's outlier columns, for the fp16 pass
+          if (kRowStash && ob[u] != 0u) s_xrow[c] = h;
+        }
       }
     }
   } else {
@@ -349,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
       // rounding per product as the MFMA form, without building 16-column
       // fragments that are almost all zero.  X values: the stashed row (one
       // row), else X itself.
-      if (!ROW || kRowStash) {
+      if (RR != 1 || kRowStash) {
         uint64_t cols = ((uint64_t)s_bits[2 * st + 1] << 32) | s_bits[2 * st];
         if (__popcll(cols) <= kSparseCols) {
           const uint32_t* slot32 = reinterpret_cast<const uint32_t*>(&s_wslot[k][0][0]);
@@ -358,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
             cols &= cols - 1ull;
             const int col = st * 64 + c;
             const int src = (lane & 15) + 16 * (c >> 4);
-            if constexpr (ROW) {
+            if constexpr (RR == 1) {
               // the single row is row 0 of the accumulator: lanes 0..15, element 0
               const float x = h2f((uint16_t)half_at(s_xrow[col >> 3], col & 7));
 #pragma unroll
@@ -485,11 +519,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
     if (MODE == 1) {
       C[(size_t)m * N + n] = csum[u];
     } else {
-      const float sc = (ROW ? ax : s_ax[m]) * s_aw[g * 16 + (ln & 15)] * kInv127Sq;
+      const float sc = (RR == 1 ? ax : s_ax[m]) * s_aw[g * 16 + (ln & 15)] * kInv127Sq;
       const float b = h2f((uint16_t)s_bias[g * 16 + (ln & 15)]);
       Y[(size_t)m * N + n] = f2h((float)csum[u] * sc + osum[u] + b);
     }
   }
+}
+
+// 16-row weight groups per workgroup: spread over the 256 CUs, 1 .. 8.
+static int decode_groups_per_workgroup(int N) {
+  const int groups = (N + 15) / 16;
+  int G = (groups + 255) / 256;
+  if (G > 8) G = 8;
+  if (G < 1) G = 1;
+  return G;
 }
 
 template <int G>
@@ -497,14 +540,18 @@ static void launch_g(dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1, con
                      int K, int ldk, const float* xs, const float* ws, const uint16_t* X,
                      const uint32_t* mb, float threshold, const uint16_t* bias, uint16_t* Y,
                      int32_t* C) {
-  if (Xq == nullptr)
-    hipExtLaunchKernelGGL((k_gemm_decode<G, 0, true>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
-                          Wq, M, N, K, ldk, xs, ws, X, mb, threshold, bias, Y, C);
-  else if (C != nullptr)
-    hipExtLaunchKernelGGL((k_gemm_decode<G, 1, false>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
+  if (Xq == nullptr) {  // the rows of X coded in the kernel
+    if (M == 1)
+      hipExtLaunchKernelGGL((k_gemm_decode<G, 0, 1>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
+                            Wq, M, N, K, ldk, xs, ws, X, mb, threshold, bias, Y, C);
+    else if constexpr (G <= kRowsMaxG)  // (gemm_decode_row_ok admits no other)
+      hipExtLaunchKernelGGL((k_gemm_decode<G, 0, 4>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
+                            Wq, M, N, K, ldk, xs, ws, X, mb, threshold, bias, Y, C);
+  } else if (C != nullptr)
+    hipExtLaunchKernelGGL((k_gemm_decode<G, 1, 0>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
                           Wq, M, N, K, ldk, xs, ws, X, mb, threshold, bias, Y, C);
   else
-    hipExtLaunchKernelGGL((k_gemm_decode<G, 0, false>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
+    hipExtLaunchKernelGGL((k_gemm_decode<G, 0, 0>), grid, dim3(kThreads), 0, s, e0, e1, 0, Xq,
                           Wq, M, N, K, ldk, xs, ws, X, mb, threshold, bias, Y, C);
 }
 
@@ -516,9 +563,7 @@ static hipError_t launch_decode(const int8_t* Xq, const int8_t* Wq, int M, int N
                                 hipEvent_t e1) {
   // Spread the 16-row groups evenly over the 256 CUs: G groups per workgroup.
   const int groups = (N + 15) / 16;
-  int G = (groups + 255) / 256;
-  if (G > 8) G = 8;
-  if (G < 1) G = 1;
+  const int G = decode_groups_per_workgroup(N);
   dim3 grid((groups + G - 1) / G);
 #define I8MM_DECODE_G(g)                                                                  \
   case g:                                                                                 \
@@ -551,17 +596,19 @@ hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, 
                        s, e0, e1);
 }
 
-bool gemm_decode_row_ok(const uint16_t* X, int M, int K, int ldk) {
-  return M == 1 && K > 0 && (K % 8) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0 &&
-         ldk <= kRowMaxLdk;
+bool gemm_decode_row_ok(const uint16_t* X, int M, int K, int ldk, int N) {
+  return M >= 1 && M <= 4 && K > 0 && (K % 8) == 0 &&
+         (reinterpret_cast<uintptr_t>(X) & 15) == 0 &&
+         ldk <= (M == 1 ? kRowMaxLdk : kRowsMaxLdk) &&
+         (M == 1 || decode_groups_per_workgroup(N) <= kRowsMaxG);
 }
 
-hipError_t launch_gemm_decode_row(const uint16_t* X, int K, int ldk, float threshold,
+hipError_t launch_gemm_decode_row(const uint16_t* X, int M, int K, int ldk, float threshold,
                                   const int8_t* Wq, int N, const float* w_scale,
                                   const uint16_t* bias, uint16_t* Y, hipStream_t s, hipEvent_t e0,
                                   hipEvent_t e1) {
-  if (!gemm_decode_row_ok(X, 1, K, ldk) || Y == nullptr) return hipErrorInvalidValue;
-  return launch_decode(nullptr, Wq, 1, N, K, ldk, nullptr, w_scale, X, nullptr, threshold, bias,
+  if (!gemm_decode_row_ok(X, M, K, ldk, N) || Y == nullptr) return hipErrorInvalidValue;
+  return launch_decode(nullptr, Wq, M, N, K, ldk, nullptr, w_scale, X, nullptr, threshold, bias,
                        Y, nullptr, s, e0, e1);
 }
 

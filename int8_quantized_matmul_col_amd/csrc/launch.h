@@ -55,11 +55,12 @@ hipError_t launch_gemm_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, 
                               const uint32_t* mask_bits, const uint16_t* bias, uint16_t* Y,
                               int32_t* C, hipStream_t s, hipEvent_t e0 = nullptr,
                               hipEvent_t e1 = nullptr);
-// One row (M == 1), Y output: the same kernel deriving the mask, a_x and the
+// One to four rows, Y output: the same kernel deriving the mask, a_x and the
 // codes of X itself, so the call is a single launch.  Applicable when
-// gemm_decode_row_ok() (K % 8 == 0, X 16-byte aligned, ldk <= 16384).
-bool gemm_decode_row_ok(const uint16_t* X, int M, int K, int ldk);
-hipError_t launch_gemm_decode_row(const uint16_t* X, int K, int ldk, float threshold,
+// gemm_decode_row_ok() (M <= 4, K % 8 == 0, X 16-byte aligned, ldk <= 16384
+// for one row, <= 8192 and N <= 28672 for two to four).
+bool gemm_decode_row_ok(const uint16_t* X, int M, int K, int ldk, int N);
+hipError_t launch_gemm_decode_row(const uint16_t* X, int M, int K, int ldk, float threshold,
                                   const int8_t* Wq, int N, const float* w_scale,
                                   const uint16_t* bias, uint16_t* Y, hipStream_t s,
                                   hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);

@@ -166,7 +166,7 @@ def ingest_pmc(config: str, fetch_dir: str, write_dir: str) -> int:
     # the Y-output instantiation timed by the bench (MODE 0), not the int32-C
     # one that the |O| probe before the timed region runs
     kname = "k_gemm_decode" if case.M <= 16 else "k_gemm_prefill"
-    kpat = re.compile(r"k_gemm_decode<\d+, 0, (?:true|false)>" if case.M <= 16 else r"k_gemm_prefill<0>")
+    kpat = re.compile(r"k_gemm_decode<\d+, 0, \d+>" if case.M <= 16 else r"k_gemm_prefill<0>")
     fetch = _pmc_means(fetch_dir, "FETCH_SIZE")
     write = _pmc_means(write_dir, "WRITE_SIZE")
 

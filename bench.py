@@ -1,6 +1,6 @@
 """Benchmark of the decomposed int8 matmul on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config sweep13b] [--extra q_proj,decode1,decode16]
+    python bench.py [--steps K] [--warmup W] [--config sweep13b] [--extra q_proj,decode1,decode4,decode16]
 
 One step = one whole int8_matmul call (activation pass: outlier detection,
 row quantization and compaction; int8 MFMA GEMM; fp16 outlier MFMA; fused
@@ -588,7 +588,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="sweep13b")
-    ap.add_argument("--extra", default="q_proj,decode1,decode16",
+    ap.add_argument("--extra", default="q_proj,decode1,decode4,decode16",
                     help="workloads measured after the headline in the same run ('none': only "
                          "the headline)")
     ap.add_argument("--threshold", type=float, default=None)

@@ -5,25 +5,29 @@
 // Work split: a workgroup owns G groups of 16 weight rows (output columns n)
 // and 8 waves split K between them.  Per 64-byte K step a wave loads one
 // 16-byte Xq fragment (rows m = lane%16, zero for m >= M) and G 16-byte Wq
-// fragments and issues G v_mfma_i32_16x16x64_i8.  When the 64-column window
-// holds an outlier column (wave-uniform test on the mask bits), the wave
-// also builds fp16 fragments of X_O (X values of the outlier columns, 0
-// elsewhere) and of W_O = fp16(fp32(Wq*a_w)/127) from the int8 bytes already
-// in registers, and accumulates them with v_mfma_f32_16x16x32_f16 into
-// separate fp32 accumulators ("LLM.int8() notes", section 2.3: FP16 outlier
-// term; "PyTorch 2.9 supports LLM.int8()", section 3: merged at the end).
-// The 8 per-wave partials are summed in LDS in a fixed order (deterministic)
-// and the epilogue writes Y = fp16(fp32(C)*a_x*a_w/127^2 + Y_O).
+// fragments and issues G v_mfma_i32_16x16x64_i8.  The Wq fragments of the
+// K steps that hold outlier columns are parked in LDS (with more than 8 such
+// steps they are used at once instead), and after the weight stream their
+// fp16 term is formed from X_O (X values of the outlier
+// columns) and W_O = fp16(fp32(Wq*a_w)/127) built from those int8 bytes
+// ("LLM.int8() notes", section 2.3: FP16 outlier term; "PyTorch 2.9 supports
+// LLM.int8()", section 3: merged at the end): a step with few outlier
+// columns with fmas straight into the accumulator layout, a denser one with
+// v_mfma_f32_16x16x32_f16 on 16-column fragments.  The 8 per-wave partials
+// are summed in LDS in a fixed order (deterministic) and the epilogue writes
+// Y = fp16(fp32(C)*a_x*a_w/127^2 + Y_O).
 //
-// Every wave's first two K steps of weight are requested at kernel entry,
-// before the set-up (mask words, outlier-step scan, barriers), so the weight
-// stream starts with the kernel.  For a single row (M = 1) the column max is
-// the row's own |x|, so each workgroup can derive the mask, a_x and the codes
-// of X by itself (a 16 KiB row, read from L2 by all but the first
-// workgroups) while those loads are in flight: the whole call is one launch,
-// with the codes held in LDS ("PyTorch 2.9 supports LLM.int8()", section 2:
-// per-row absmax scale of the activations; "LLM.int8() notes", section 3.2:
-// outlier columns are those whose magnitude exceeds the threshold).
+// The small loads of the set-up (scales, mask words or rows of X) are
+// requested first at kernel entry, then every wave's first two K steps of
+// weight, so the weight stream starts with the kernel and the set-up
+// (mask words, outlier-step scan, barriers) runs while it arrives.  For up
+// to four rows each workgroup derives the mask (column maxima over the
+// rows), a_x and the codes of X by itself (16 KiB per row, read from L2 by
+// all but the first workgroups) while those loads are in flight: the whole
+// call is one launch, with the codes held in LDS ("PyTorch 2.9 supports
+// LLM.int8()", section 2: per-row absmax scale of the activations; "LLM.int8()
+// notes", section 3.2: outlier columns are those whose magnitude exceeds the
+// threshold).
 #include "device_common.h"
 #include "launch.h"
 #include "tile_layout.h"
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_decode(
   // the whole chunk had arrived (and the next chunk is requested only after
   // the set-up).  The scales and biases the fp16 outlier pass and the
   // epilogue need (one value per thread, into LDS at the set-up's barrier),
-  // the first mask words (activation pass) or the row of X (single row).
+  // the first mask words (activation pass) or the rows of X (coded here).
   const int sn = min(n_base + t, N - 1);
   const float pre_aw = t < G * 16 ? w_scale[sn] : 0.0f;
   // (the bias as its bits, converted where it is used: a conversion here
@@ -555,7 +559,7 @@ static void launch_g(dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1, con
                           Wq, M, N, K, ldk, xs, ws, X, mb, threshold, bias, Y, C);
 }
 
-// Xq == nullptr: the single-row form that codes X itself (M == 1, Y output).
+// Xq == nullptr: the form that codes the rows of X itself (M <= 4, Y output).
 static hipError_t launch_decode(const int8_t* Xq, const int8_t* Wq, int M, int N, int K, int ldk,
                                 const float* x_scale, const float* w_scale, const uint16_t* X,
                                 const uint32_t* mask_bits, float threshold, const uint16_t* bias,

@@ -58,6 +58,12 @@ SHAPES = [
     (2, 200, 33, 3, math.inf),
     (4, 512, 32784, 3, 6.0),
     (3, 8200, 64, 3, 6.0),
+    # two to four rows coded inside the decode kernel (ldk <= 8192, up to 7
+    # weight groups per workgroup): three rows (the fourth repeats the
+    # third), two rows over 3 groups per workgroup, four rows at ldk = 8192
+    (3, 4096, 700, 5, 6.0),
+    (2, 1024, 8704, 3, 6.0),
+    (4, 8192, 96, 6, 6.0),
     # prefill path: M > 16
     (17, 1024, 1024, 2, 6.0),
     (300, 520, 300, 5, 6.0),
